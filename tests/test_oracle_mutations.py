@@ -1,0 +1,106 @@
+"""Plants plausible mistakes in the oracle (on the CPU, through monkeypatching) and checks
+that at least one pin fails for each: the pins are able to catch a dropped term, a wrong
+sign or index, a transposed operand or a flipped tie rule."""
+import numpy as np
+import pytest
+
+import oracle.attention as OA
+import oracle.flashblock as OF
+import oracle.losa as OL
+import tests.test_oracle_attention as TA
+import tests.test_oracle_flashblock as TF
+import tests.test_oracle_losa as TL
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except (AssertionError, ValueError, IndexError):
+        return True
+    return False
+
+
+def test_merge_with_swapped_weights_is_caught(monkeypatch):
+    def bad(a1, l1, a2, l2):
+        return _orig_merge(a1, l2, a2, l1)
+    _orig_merge = OA.lse_merge
+    monkeypatch.setattr(TA, "lse_merge", bad)
+    assert _fails(TA.test_golden_two_key_merge)
+
+
+def test_attend_without_scale_is_caught(monkeypatch):
+    orig = OA.attend
+    monkeypatch.setattr(TA, "attend", lambda q, k, v, s: orig(q, k, v, 1.0))
+    assert _fails(TA.test_attend_matches_torch_sdpa_fp64)
+
+
+def test_attend_with_transposed_value_use_is_caught(monkeypatch):
+    def bad(q, k, v, scale):
+        a, l = OA.attend(q, v, k, scale)       # keys and values swapped
+        return a, l
+    monkeypatch.setattr(TA, "attend", bad)
+    assert _fails(TA.test_attend_closed_forms)
+
+
+def test_wrong_gqa_mapping_is_caught(monkeypatch):
+    monkeypatch.setattr(OA, "_kv_head", lambda h, hq, hkv: h % hkv)
+    assert _fails(TA.test_multihead_layouts_brute_force, 3, 2, 8, 2, 3, [2, 7, 4])
+
+
+def test_merge_dropping_log_term_is_caught(monkeypatch):
+    def bad(a1, l1, a2, l2):
+        a, l = _orig(a1, l1, a2, l2)
+        return a, np.maximum(l1, l2)           # forgets + log(w1 + w2)
+    _orig = OA.lse_merge
+    monkeypatch.setattr(TA, "lse_merge", bad)
+    assert _fails(TA.test_merge_conventions)
+
+
+def test_threshold_non_strict_is_caught(monkeypatch):
+    monkeypatch.setattr(TF, "mask_threshold",
+                        lambda m, tau, hq: np.repeat((np.asarray(m) <= tau).astype(np.uint8)[:, None], hq, 1))
+    assert _fails(TF.test_golden_reuse_rules)
+
+
+def test_reuse_that_rewrites_cache_is_caught(monkeypatch):
+    def bad(q, k, v, cu, kb, vb, mask, ca, cl, scale):
+        return OF.step(q, k, v, cu, kb, vb, np.zeros_like(mask), ca, cl, scale)
+    monkeypatch.setattr(TF, "step", bad)
+    assert _fails(TF.test_reuse_step_semantics)
+
+
+def test_topk_tie_to_higher_index_is_caught(monkeypatch):
+    def bad(S, k):
+        S = np.asarray(S, dtype=np.float64)
+        R, P = S.shape
+        out = np.full((R, k), -1, dtype=np.int32)
+        for r in range(R):
+            order = np.lexsort((-np.arange(P), -S[r]))[:k]
+            out[r, :order.size] = np.sort(order)
+        return out
+    monkeypatch.setattr(OL, "topk_pages", bad)
+    assert _fails(TL.test_topk_brute_force_with_ties)
+
+
+def test_quest_min_only_is_caught(monkeypatch):
+    def bad(qa, kmin, kmax):
+        return _orig(qa, kmin, kmin)
+    _orig = OL.quest_scores
+    monkeypatch.setattr(OL, "quest_scores", bad)
+    assert _fails(TL.test_quest_exact_rational_and_bound)
+
+
+def test_locality_wrong_sign_is_caught(monkeypatch):
+    def bad(qc, qp):
+        x, y = np.asarray(qc, float), np.asarray(qp, float)
+        return ((x + y) ** 2).mean(axis=(2, 3))
+    monkeypatch.setattr(OL, "locality_scores", bad)
+    assert _fails(TL.test_golden_locality)
+
+
+def test_active_set_tie_to_higher_index_is_caught(monkeypatch):
+    def bad(scores, n):
+        s = np.asarray(scores)
+        return np.array([np.sort(sorted(range(s.shape[1]), key=lambda i: (-s[b, i], -i))[:n]) for b in range(s.shape[0])])
+    monkeypatch.setattr(OL, "active_set", bad)
+    assert _fails(TL.test_active_set_ties_and_order)
