@@ -1,0 +1,489 @@
+// Host side of the C ABI declared in include/flashblock.h: argument validation (before
+// anything is enqueued), the shape-only split plan, workspace carving and launches.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/flashblock.h"
+#include "fb_internal.hpp"
+
+using namespace fb;
+
+namespace {
+
+constexpr int kTileKeys = 128;       // key tile of the bf16 attention kernel
+constexpr int kTargetItems = 1024;   // workgroups the split plan aims for (256 CUs x 4)
+constexpr int kMinChunk = 512;       // smallest automatic chunk (keys)
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+fb_status check_shape(const fb_shape* s) {
+  if (!s) return FB_ERR_INVALID_ARG;
+  if (s->batch < 1 || s->h_q < 1 || s->h_kv < 1 || s->head_dim < 1 || s->block < 1) return FB_ERR_INVALID_ARG;
+  if (s->h_q % s->h_kv != 0) return FB_ERR_INVALID_ARG;
+  if (s->flags != 0 || s->num_splits < 0) return FB_ERR_INVALID_ARG;
+  if (!(s->softmax_scale >= 0.f) || !isfinite(s->softmax_scale)) return FB_ERR_INVALID_ARG;
+  if (s->cu_seqlens_k ? s->max_seqlen_k < 0 : s->seqlen_k < 0) return FB_ERR_INVALID_ARG;
+  if (s->dtype == FB_BF16) {
+    if (s->head_dim != 64 && s->head_dim != 128) return FB_ERR_UNSUPPORTED;
+  } else if (s->dtype == FB_F32) {
+    if (s->head_dim > 256) return FB_ERR_UNSUPPORTED;
+  } else {
+    return FB_ERR_INVALID_ARG;
+  }
+  const int64_t rows = (int64_t)s->batch * s->block * s->h_q;
+  if (rows * s->head_dim >= ((int64_t)1 << 40)) return FB_ERR_UNSUPPORTED;
+  if (s->batch > 65535) return FB_ERR_UNSUPPORTED;                       // grid z
+  // grid y = h_kv * query groups (at least 32 rows each)
+  if ((int64_t)s->h_kv * cdiv((int64_t)(s->h_q / s->h_kv) * s->block, 32) > 65535) return FB_ERR_UNSUPPORTED;
+  return FB_OK;
+}
+
+inline int max_prefix(const fb_shape* s) { return s->cu_seqlens_k ? s->max_seqlen_k : s->seqlen_k; }
+inline float scale_of(const fb_shape* s) {
+  return s->softmax_scale > 0.f ? s->softmax_scale : 1.0f / sqrtf((float)s->head_dim);
+}
+
+// Rows of a (sequence, KV head) group and how the attention kernel tiles them.
+struct RowPlan {
+  int rows, rows_per_head, tq, qgroups;
+};
+RowPlan row_plan(const fb_shape* s, int rows_per_head) {
+  RowPlan r;
+  r.rows_per_head = rows_per_head;
+  r.rows = (s->h_q / s->h_kv) * rows_per_head;
+  if (s->dtype == FB_BF16)
+    r.tq = r.rows <= 32 ? 1 : (r.rows <= 64 ? 2 : 4);
+  else
+    r.tq = 1;
+  r.qgroups = (int)cdiv(r.rows, 32 * r.tq);
+  return r;
+}
+
+// Key chunking of one source: depends on the shape only (deterministic results).
+struct SplitPlan {
+  int chunk, splits;
+};
+SplitPlan split_plan(const fb_shape* s, const RowPlan& rp, int64_t max_keys, int forced) {
+  SplitPlan p;
+  if (max_keys <= 0) {
+    p.chunk = kTileKeys;
+    p.splits = 0;
+    return p;
+  }
+  int64_t want;
+  if (forced > 0) {
+    want = forced;
+  } else {
+    const int64_t items = (int64_t)s->batch * s->h_kv * rp.qgroups;
+    want = cdiv(kTargetItems, items);
+  }
+  int64_t chunk = round_up(cdiv(max_keys, want), kTileKeys);
+  if (forced <= 0 && chunk < kMinChunk) chunk = kMinChunk < round_up(max_keys, kTileKeys) ? kMinChunk : round_up(max_keys, kTileKeys);
+  p.chunk = (int)chunk;
+  p.splits = (int)cdiv(max_keys, chunk);
+  return p;
+}
+
+struct Region {
+  size_t o_off, ml_off, bytes;
+};
+Region partial_region(const fb_shape* s, const RowPlan& rp, const SplitPlan& sp, size_t base) {
+  Region r;
+  const size_t slots = (size_t)s->batch * s->h_kv * sp.splits;
+  r.o_off = base;
+  r.ml_off = align256(base + slots * rp.rows * s->head_dim * sizeof(float));
+  r.bytes = align256(r.ml_off + slots * rp.rows * 2 * sizeof(float)) - base;
+  return r;
+}
+
+// Full plan of the dense step (prefix source 0, block source 1).
+struct StepPlan {
+  RowPlan rp;
+  SplitPlan pre, blk;
+  Region rpre, rblk;
+  size_t ws_bytes;
+};
+StepPlan step_plan(const fb_shape* s) {
+  StepPlan p;
+  p.rp = row_plan(s, s->block);
+  p.pre = split_plan(s, p.rp, max_prefix(s), s->num_splits);
+  p.blk = split_plan(s, p.rp, s->block, 0);
+  p.rpre = partial_region(s, p.rp, p.pre, 0);
+  p.rblk = partial_region(s, p.rp, p.blk, p.rpre.bytes);
+  p.ws_bytes = p.rpre.bytes + p.rblk.bytes;
+  return p;
+}
+
+AttnSrc make_src(const RowPlan& rp, const SplitPlan& sp, const void* k, const void* v, const int32_t* cu,
+                 int n_uniform, float* ws, const Region& reg) {
+  AttnSrc a;
+  memset(&a, 0, sizeof(a));
+  a.k = k;
+  a.v = v;
+  a.cu = cu;
+  a.n_uniform = n_uniform;
+  a.chunk = sp.chunk;
+  a.n_splits = sp.splits;
+  a.rows_per_head = rp.rows_per_head;
+  a.rows = rp.rows;
+  a.tq = rp.tq;
+  a.qgroups = rp.qgroups;
+  a.po = (float*)((char*)ws + reg.o_off);
+  a.pml = (float*)((char*)ws + reg.ml_off);
+  return a;
+}
+
+AttnArgs base_args(const fb_shape* s, const void* q) {
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.batch = s->batch;
+  a.B = s->block;
+  a.h_q = s->h_q;
+  a.h_kv = s->h_kv;
+  a.G = s->h_q / s->h_kv;
+  a.d = s->head_dim;
+  a.scale_log2 = scale_of(s) * 1.4426950408889634f;
+  return a;
+}
+
+CombineArgs base_combine(const fb_shape* s, const StepPlan& p, float* ws) {
+  CombineArgs c;
+  memset(&c, 0, sizeof(c));
+  c.batch = s->batch;
+  c.B = s->block;
+  c.h_q = s->h_q;
+  c.h_kv = s->h_kv;
+  c.G = s->h_q / s->h_kv;
+  c.d = s->head_dim;
+  c.po = (const float*)((char*)ws + p.rpre.o_off);
+  c.pml = (const float*)((char*)ws + p.rpre.ml_off);
+  c.p_rows = p.rp.rows;
+  c.p_splits = p.pre.splits;
+  c.p_chunk = p.pre.chunk;
+  c.cu = s->cu_seqlens_k;
+  c.n_uniform = s->seqlen_k;
+  c.bo = (const float*)((char*)ws + p.rblk.o_off);
+  c.bml = (const float*)((char*)ws + p.rblk.ml_off);
+  c.b_rows = p.rp.rows;
+  c.b_splits = p.blk.splits;
+  c.b_chunk = p.blk.chunk;
+  c.out_bf16 = s->dtype == FB_BF16;
+  return c;
+}
+
+bool prefix_may_be_empty(const fb_shape* s) { return !s->cu_seqlens_k && s->seqlen_k == 0; }
+
+fb_status check_inputs(const fb_shape* s, const void* q, const void* k, const void* v) {
+  if (!q || !aligned16(q)) return FB_ERR_INVALID_ARG;
+  if (!prefix_may_be_empty(s) && (!k || !v || !aligned16(k) || !aligned16(v))) return FB_ERR_INVALID_ARG;
+  return FB_OK;
+}
+
+inline void rec(hipEvent_t e, hipStream_t st) {
+  if (e) hipEventRecord(e, st);
+}
+
+fb_status hip_status(hipError_t e) { return e == hipSuccess ? FB_OK : FB_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fb_status_string(fb_status s) {
+  switch (s) {
+    case FB_OK: return "ok";
+    case FB_ERR_INVALID_ARG: return "invalid argument";
+    case FB_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FB_ERR_WORKSPACE: return "workspace too small";
+    case FB_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+size_t fb_workspace_size(const fb_shape* s) {
+  if (check_shape(s) != FB_OK) return 0;
+  return step_plan(s).ws_bytes;
+}
+
+fb_status fb_prefix_attn(const fb_shape* s, const void* q, const void* k, const void* v, float* a_out,
+                         float* l_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  fb_status st = check_shape(s);
+  if (st != FB_OK) return st;
+  if ((st = check_inputs(s, q, k, v)) != FB_OK) return st;
+  if (!a_out || !l_out) return FB_ERR_INVALID_ARG;
+  const StepPlan p = step_plan(s);
+  if (ws_bytes < p.ws_bytes || (p.ws_bytes && (!ws || !aligned16(ws)))) return FB_ERR_WORKSPACE;
+  AttnArgs a = base_args(s, q);
+  a.src0 = make_src(p.rp, p.pre, k, v, s->cu_seqlens_k, s->seqlen_k, (float*)ws, p.rpre);
+  if (hipError_t e = launch_attn(a, s->dtype == FB_BF16, stream)) return hip_status(e);
+  CombineArgs c = base_combine(s, p, (float*)ws);
+  c.mode = kModePrefixOnly;
+  c.cache_a = a_out;
+  c.cache_l = l_out;
+  return hip_status(launch_combine(c, stream));
+}
+
+fb_status fb_block_attn(const fb_shape* s, const void* q, const void* k_blk, const void* v_blk, float* a_in,
+                        float* l_in, void* ws, size_t ws_bytes, hipStream_t stream) {
+  fb_status st = check_shape(s);
+  if (st != FB_OK) return st;
+  if (!q || !k_blk || !v_blk || !aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk)) return FB_ERR_INVALID_ARG;
+  if (!a_in || !l_in) return FB_ERR_INVALID_ARG;
+  const StepPlan p = step_plan(s);
+  if (ws_bytes < p.ws_bytes || (p.ws_bytes && (!ws || !aligned16(ws)))) return FB_ERR_WORKSPACE;
+  AttnArgs a = base_args(s, q);
+  a.src1 = make_src(p.rp, p.blk, k_blk, v_blk, nullptr, s->block, (float*)ws, p.rblk);
+  if (hipError_t e = launch_attn(a, s->dtype == FB_BF16, stream)) return hip_status(e);
+  CombineArgs c = base_combine(s, p, (float*)ws);
+  c.mode = kModeBlockOnly;
+  c.ain = a_in;
+  c.lin = l_in;
+  return hip_status(launch_combine(c, stream));
+}
+
+fb_status fb_lse_merge(int64_t rows, int32_t d, const float* a_out, const float* l_out, const float* a_in,
+                       const float* l_in, void* a_full, fb_dtype out_dtype, float* l_full, hipStream_t stream) {
+  if (rows < 0 || d < 1 || d > 256) return rows < 0 || d < 1 ? FB_ERR_INVALID_ARG : FB_ERR_UNSUPPORTED;
+  if (out_dtype != FB_BF16 && out_dtype != FB_F32) return FB_ERR_INVALID_ARG;
+  if (rows == 0) return FB_OK;
+  if (!a_out || !l_out || !a_in || !l_in || !a_full) return FB_ERR_INVALID_ARG;
+  return hip_status(launch_lse_merge(rows, d, a_out, l_out, a_in, l_in, a_full, out_dtype == FB_BF16, l_full, stream));
+}
+
+fb_status fb_step(const fb_shape* s, const void* q, const void* k, const void* v, const void* k_blk,
+                  const void* v_blk, const uint8_t* reuse_mask, float* cache_a, float* cache_l, void* a_full,
+                  float* l_full, void* ws, size_t ws_bytes, const fb_trace* trace, hipStream_t stream) {
+  fb_status st = check_shape(s);
+  if (st != FB_OK) return st;
+  if ((st = check_inputs(s, q, k, v)) != FB_OK) return st;
+  if (!k_blk || !v_blk || !aligned16(k_blk) || !aligned16(v_blk)) return FB_ERR_INVALID_ARG;
+  if (!cache_a || !cache_l || !a_full) return FB_ERR_INVALID_ARG;
+  const StepPlan p = step_plan(s);
+  if (ws_bytes < p.ws_bytes || (p.ws_bytes && (!ws || !aligned16(ws)))) return FB_ERR_WORKSPACE;
+  AttnArgs a = base_args(s, q);
+  a.src0 = make_src(p.rp, p.pre, k, v, s->cu_seqlens_k, s->seqlen_k, (float*)ws, p.rpre);
+  a.src0.mask = reuse_mask;
+  a.src1 = make_src(p.rp, p.blk, k_blk, v_blk, nullptr, s->block, (float*)ws, p.rblk);
+  rec(trace ? trace->attn_begin : nullptr, stream);
+  if (hipError_t e = launch_attn(a, s->dtype == FB_BF16, stream)) return hip_status(e);
+  rec(trace ? trace->attn_end : nullptr, stream);
+  CombineArgs c = base_combine(s, p, (float*)ws);
+  c.mode = kModeStep;
+  c.mask = reuse_mask;
+  c.cache_a = cache_a;
+  c.cache_l = cache_l;
+  c.a_full = a_full;
+  c.l_full = l_full;
+  rec(trace ? trace->merge_begin : nullptr, stream);
+  if (hipError_t e = launch_combine(c, stream)) return hip_status(e);
+  rec(trace ? trace->merge_end : nullptr, stream);
+  return FB_OK;
+}
+
+fb_status fb_mask_threshold(const int32_t* m_updated, int32_t tau, int32_t batch, int32_t h_q, uint8_t* mask,
+                            hipStream_t stream) {
+  if (!m_updated || !mask || batch < 1 || h_q < 1) return FB_ERR_INVALID_ARG;
+  return hip_status(launch_mask_threshold(m_updated, tau, batch, h_q, mask, stream));
+}
+
+fb_status fb_mask_similarity(const float* sim, float gamma, int64_t n, uint8_t* mask, hipStream_t stream) {
+  if (n < 0 || (n > 0 && (!sim || !mask))) return FB_ERR_INVALID_ARG;
+  return hip_status(launch_mask_similarity(sim, gamma, n, mask, stream));
+}
+
+fb_status fb_head_cosine(int32_t batch, int32_t block, int32_t h_q, int32_t head_dim, const float* a_prev,
+                         const float* a_cur, float* sim, hipStream_t stream) {
+  if (batch < 1 || block < 1 || h_q < 1 || head_dim < 1 || !a_prev || !a_cur || !sim) return FB_ERR_INVALID_ARG;
+  return hip_status(launch_head_cosine(batch, block, h_q, head_dim, a_prev, a_cur, sim, stream));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------
+// LoSA-style sparse path
+// ---------------------------------------------------------------------------------------
+namespace {
+
+fb_status check_losa(const losa_shape* ls) {
+  if (!ls) return FB_ERR_INVALID_ARG;
+  fb_status st = check_shape(&ls->s);
+  if (st != FB_OK) return st;
+  const fb_shape& s = ls->s;
+  if (ls->page_size < 1 || ls->topk < 1 || ls->n_active < 1 || ls->max_pages < 1) return FB_ERR_INVALID_ARG;
+  if (ls->n_active > s.block) return FB_ERR_INVALID_ARG;
+  if (s.block > 1024 || ls->max_pages > 16384 || s.head_dim % 8 != 0) return FB_ERR_UNSUPPORTED;
+  if (cdiv(max_prefix(&s), ls->page_size) > ls->max_pages) return FB_ERR_INVALID_ARG;
+  return FB_OK;
+}
+
+int union_cap(const losa_shape* ls) {
+  const int64_t g = ls->s.h_q / ls->s.h_kv;
+  const int64_t c = (int64_t)ls->n_active * g * ls->topk;
+  return (int)(c < ls->max_pages ? c : ls->max_pages);
+}
+
+LosaArgs losa_args(const losa_shape* ls) {
+  LosaArgs a;
+  const fb_shape& s = ls->s;
+  a.batch = s.batch;
+  a.B = s.block;
+  a.h_q = s.h_q;
+  a.h_kv = s.h_kv;
+  a.G = s.h_q / s.h_kv;
+  a.d = s.head_dim;
+  a.cu = s.cu_seqlens_k;
+  a.n_uniform = s.seqlen_k;
+  a.page_size = ls->page_size;
+  a.topk = ls->topk;
+  a.n_active = ls->n_active;
+  a.max_pages = ls->max_pages;
+  a.max_union = union_cap(ls);
+  a.bf16 = s.dtype == FB_BF16;
+  return a;
+}
+
+struct LosaPlan {
+  StepPlan dense;        // block source and row plan of all B rows
+  RowPlan rp_sparse;
+  SplitPlan sp_sparse;
+  Region r_sparse, r_block;
+  size_t scores_off, active_off, ws_bytes;
+};
+LosaPlan losa_plan(const losa_shape* ls) {
+  LosaPlan p;
+  const fb_shape* s = &ls->s;
+  p.dense = step_plan(s);
+  p.rp_sparse = row_plan(s, ls->n_active);
+  p.sp_sparse = split_plan(s, p.rp_sparse, (int64_t)union_cap(ls) * ls->page_size, s->num_splits);
+  p.r_sparse = partial_region(s, p.rp_sparse, p.sp_sparse, 0);
+  p.r_block = partial_region(s, p.dense.rp, p.dense.blk, p.r_sparse.bytes);
+  p.scores_off = p.r_sparse.bytes + p.r_block.bytes;
+  const size_t scores = (size_t)s->batch * s->h_q * ls->n_active * ls->max_pages * sizeof(double);
+  p.active_off = align256(p.scores_off + scores);
+  p.ws_bytes = align256(p.active_off + (size_t)s->batch * ls->n_active * sizeof(int32_t));
+  return p;
+}
+
+fb_status run_selection(const losa_shape* ls, const LosaPlan& p, const void* q_cur, const void* q_prev,
+                        const void* kmin, const void* kmax, int32_t* active, int32_t* topk_pages,
+                        int32_t* union_pages, int32_t* union_count, void* ws, hipStream_t stream) {
+  const LosaArgs la = losa_args(ls);
+  double* scores = (double*)((char*)ws + p.scores_off);
+  if (hipError_t e = launch_locality(la, q_cur, q_prev, active, stream)) return hip_status(e);
+  if (hipError_t e = launch_quest_scores(la, q_cur, active, kmin, kmax, scores, stream)) return hip_status(e);
+  if (hipError_t e = launch_topk(la, scores, topk_pages, stream)) return hip_status(e);
+  return hip_status(launch_union(la, topk_pages, union_pages, union_count, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t losa_meta_bytes(const losa_shape* ls) {
+  if (check_losa(ls) != FB_OK) return 0;
+  const size_t el = ls->s.dtype == FB_BF16 ? 2 : 4;
+  return (size_t)ls->s.batch * ls->s.h_kv * ls->s.head_dim * ls->max_pages * el;
+}
+
+size_t losa_workspace_size(const losa_shape* ls) {
+  if (check_losa(ls) != FB_OK) return 0;
+  return losa_plan(ls).ws_bytes;
+}
+
+int32_t losa_union_capacity(const losa_shape* ls) {
+  if (check_losa(ls) != FB_OK) return 0;
+  return union_cap(ls);
+}
+
+fb_status losa_page_meta(const losa_shape* ls, const void* k, void* kmin, void* kmax, hipStream_t stream) {
+  fb_status st = check_losa(ls);
+  if (st != FB_OK) return st;
+  if (!kmin || !kmax || !aligned16(kmin) || !aligned16(kmax)) return FB_ERR_INVALID_ARG;
+  if (!k && !prefix_may_be_empty(&ls->s)) return FB_ERR_INVALID_ARG;
+  return hip_status(launch_page_meta(losa_args(ls), k, kmin, kmax, stream));
+}
+
+fb_status losa_select_union(const losa_shape* ls, const void* q_cur, const void* q_prev, const void* kmin,
+                            const void* kmax, int32_t* active, int32_t* topk_pages, int32_t* union_pages,
+                            int32_t* union_count, void* ws, size_t ws_bytes, hipStream_t stream) {
+  fb_status st = check_losa(ls);
+  if (st != FB_OK) return st;
+  if (!q_cur || !q_prev || !kmin || !kmax || !aligned16(kmin) || !aligned16(kmax)) return FB_ERR_INVALID_ARG;
+  if (!active || !topk_pages || !union_pages || !union_count) return FB_ERR_INVALID_ARG;
+  const LosaPlan p = losa_plan(ls);
+  if (ws_bytes < p.ws_bytes || !ws || !aligned16(ws)) return FB_ERR_WORKSPACE;
+  return run_selection(ls, p, q_cur, q_prev, kmin, kmax, active, topk_pages, union_pages, union_count, ws, stream);
+}
+
+fb_status losa_step(const losa_shape* ls, const void* q_cur, const void* q_prev, const void* k, const void* v,
+                    const void* k_blk, const void* v_blk, const void* kmin, const void* kmax, float* cache_a,
+                    float* cache_l, void* a_full, float* l_full, int32_t* active, int32_t* topk_pages,
+                    int32_t* union_pages, int32_t* union_count, void* ws, size_t ws_bytes,
+                    const fb_trace* trace, hipStream_t stream) {
+  fb_status st = check_losa(ls);
+  if (st != FB_OK) return st;
+  const fb_shape* s = &ls->s;
+  if ((st = check_inputs(s, q_cur, k, v)) != FB_OK) return st;
+  if (!q_prev || !kmin || !kmax || !aligned16(kmin) || !aligned16(kmax)) return FB_ERR_INVALID_ARG;
+  if (!k_blk || !v_blk || !aligned16(k_blk) || !aligned16(v_blk)) return FB_ERR_INVALID_ARG;
+  if (!cache_a || !cache_l || !a_full || !active || !topk_pages || !union_pages || !union_count)
+    return FB_ERR_INVALID_ARG;
+  const LosaPlan p = losa_plan(ls);
+  if (ws_bytes < p.ws_bytes || !ws || !aligned16(ws)) return FB_ERR_WORKSPACE;
+
+  rec(trace ? trace->select_begin : nullptr, stream);
+  st = run_selection(ls, p, q_cur, q_prev, kmin, kmax, active, topk_pages, union_pages, union_count, ws, stream);
+  if (st != FB_OK) return st;
+  rec(trace ? trace->select_end : nullptr, stream);
+
+  AttnArgs a = base_args(s, q_cur);
+  a.src0 = make_src(p.rp_sparse, p.sp_sparse, k, v, s->cu_seqlens_k, s->seqlen_k, (float*)ws, p.r_sparse);
+  a.src0.pages = union_pages;
+  a.src0.page_count = union_count;
+  a.src0.page_size = ls->page_size;
+  a.src0.max_union = union_cap(ls);
+  a.src0.row_tok = active;
+  a.src1 = make_src(p.dense.rp, p.dense.blk, k_blk, v_blk, nullptr, s->block, (float*)ws, p.r_block);
+  rec(trace ? trace->attn_begin : nullptr, stream);
+  if (hipError_t e = launch_attn(a, s->dtype == FB_BF16, stream)) return hip_status(e);
+  rec(trace ? trace->attn_end : nullptr, stream);
+
+  CombineArgs c;
+  memset(&c, 0, sizeof(c));
+  c.mode = kModeLosa;
+  c.batch = s->batch;
+  c.B = s->block;
+  c.h_q = s->h_q;
+  c.h_kv = s->h_kv;
+  c.G = s->h_q / s->h_kv;
+  c.d = s->head_dim;
+  c.po = (const float*)((char*)ws + p.r_sparse.o_off);
+  c.pml = (const float*)((char*)ws + p.r_sparse.ml_off);
+  c.p_rows = p.rp_sparse.rows;
+  c.p_splits = p.sp_sparse.splits;
+  c.p_chunk = p.sp_sparse.chunk;
+  c.page_count = union_count;
+  c.page_size = ls->page_size;
+  c.bo = (const float*)((char*)ws + p.r_block.o_off);
+  c.bml = (const float*)((char*)ws + p.r_block.ml_off);
+  c.b_rows = p.dense.rp.rows;
+  c.b_splits = p.dense.blk.splits;
+  c.b_chunk = p.dense.blk.chunk;
+  c.active = active;
+  c.n_active = ls->n_active;
+  c.cache_a = cache_a;
+  c.cache_l = cache_l;
+  c.a_full = a_full;
+  c.l_full = l_full;
+  c.out_bf16 = s->dtype == FB_BF16;
+  rec(trace ? trace->merge_begin : nullptr, stream);
+  if (hipError_t e = launch_combine(c, stream)) return hip_status(e);
+  rec(trace ? trace->merge_end : nullptr, stream);
+  return FB_OK;
+}
+
+}  // extern "C"

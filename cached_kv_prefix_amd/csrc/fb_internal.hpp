@@ -1,0 +1,92 @@
+// Internal job descriptors shared by the host launchers and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fb {
+
+// One key source of the attention kernel.  Keys of sequence b are the tokens
+//   contiguous:  seq0(b) + key,                          key < count(b)
+//   paged:       seq0(b) + pages[b][hk][key / P] * P + key % P,
+//                key < page_count[b][hk] * P, masked when the token is >= N_b
+// with seq0(b) = cu ? cu[b] : b * n_uniform and count(b) = cu ? cu[b+1]-cu[b] : n_uniform.
+// Rows of a (b, hk) group: r = j * rows_per_head + i for the group's j-th query head and
+// row i, where i is the block token itself or row_tok[b][i] when row_tok is set.
+struct AttnSrc {
+  const void* k;
+  const void* v;
+  const int32_t* cu;
+  int32_t n_uniform;
+  const int32_t* pages;       // paged source (LoSA union), else null
+  const int32_t* page_count;  // [batch][h_kv]
+  int32_t page_size;
+  int32_t max_union;
+  int32_t chunk;              // keys per split (multiple of 128)
+  int32_t n_splits;           // grid extent along x for this source
+  int32_t rows_per_head;
+  const int32_t* row_tok;     // [batch][rows_per_head] or null
+  int32_t rows;               // G * rows_per_head
+  int32_t tq;                 // 32-row query tiles per workgroup (1, 2 or 4)
+  int32_t qgroups;            // ceil(rows / (32 * tq))
+  const uint8_t* mask;        // [batch][h_q]: skip a workgroup whose heads all reuse
+  float* po;                  // partial O   [batch][h_kv][n_splits][rows][d]
+  float* pml;                 // partial m,l [batch][h_kv][n_splits][rows][2]
+};
+
+struct AttnArgs {
+  const void* q;              // [batch][B][h_q][d]
+  int32_t batch, B, h_q, h_kv, G, d;
+  float scale_log2;           // softmax_scale * log2(e)
+  AttnSrc src0, src1;         // grid x: [0, src0.n_splits) then [.., + src1.n_splits)
+};
+
+enum CombineMode { kModeStep = 0, kModePrefixOnly = 1, kModeBlockOnly = 2, kModeLosa = 3 };
+
+struct CombineArgs {
+  int32_t mode;
+  int32_t batch, B, h_q, h_kv, G, d;
+  // prefix partials (src0) and how many splits of each group are valid
+  const float* po; const float* pml; int32_t p_rows; int32_t p_splits; int32_t p_chunk;
+  const int32_t* cu; int32_t n_uniform;
+  const int32_t* page_count; int32_t page_size;
+  // block partials (src1)
+  const float* bo; const float* bml; int32_t b_rows; int32_t b_splits; int32_t b_chunk;
+  const uint8_t* mask;                 // step: [batch][h_q], null = recompute all
+  const int32_t* active; int32_t n_active;   // LoSA
+  float* cache_a; float* cache_l;      // step/LoSA cache, or prefix-only outputs
+  float* ain; float* lin;              // block-only outputs
+  void* a_full; int32_t out_bf16; float* l_full;
+};
+
+hipError_t launch_attn(const AttnArgs& a, bool bf16, hipStream_t st);
+hipError_t launch_combine(const CombineArgs& c, hipStream_t st);
+hipError_t launch_lse_merge(int64_t rows, int32_t d, const float* ao, const float* lo,
+                            const float* ai, const float* li, void* af, int out_bf16,
+                            float* lf, hipStream_t st);
+hipError_t launch_mask_threshold(const int32_t* m, int32_t tau, int32_t batch, int32_t h_q,
+                                 uint8_t* mask, hipStream_t st);
+hipError_t launch_mask_similarity(const float* sim, float gamma, int64_t n, uint8_t* mask,
+                                  hipStream_t st);
+hipError_t launch_head_cosine(int32_t batch, int32_t B, int32_t h_q, int32_t d,
+                              const float* a0, const float* a1, float* sim, hipStream_t st);
+
+// LoSA selection
+struct LosaArgs {
+  int32_t batch, B, h_q, h_kv, G, d;
+  const int32_t* cu; int32_t n_uniform;
+  int32_t page_size, topk, n_active, max_pages, max_union;
+  int32_t bf16;
+};
+hipError_t launch_page_meta(const LosaArgs& a, const void* k, void* kmin, void* kmax,
+                            hipStream_t st);
+hipError_t launch_locality(const LosaArgs& a, const void* qc, const void* qp,
+                           int32_t* active, hipStream_t st);
+hipError_t launch_quest_scores(const LosaArgs& a, const void* qc, const int32_t* active,
+                               const void* kmin, const void* kmax, double* scores,
+                               hipStream_t st);
+hipError_t launch_topk(const LosaArgs& a, const double* scores, int32_t* topk_pages,
+                       hipStream_t st);
+hipError_t launch_union(const LosaArgs& a, const int32_t* topk_pages, int32_t* union_pages,
+                        int32_t* union_count, hipStream_t st);
+
+}  // namespace fb

@@ -76,13 +76,13 @@ def page_minmax(k, cu, page: int):
         lo, hi = int(cu[bi]), int(cu[bi + 1])
         n = hi - lo
         P = page_count(n, page)
-        kk = np.asarray(k[lo:hi], dtype=np.float64)
+        kk = k[lo:hi]              # min / max are exact in the input precision
         mn = np.zeros((P, kk.shape[1], kk.shape[2]))
         mx = np.zeros_like(mn)
         for p in range(P):
             seg = kk[p * page:min((p + 1) * page, n)]
-            mn[p] = seg.min(axis=0)
-            mx[p] = seg.max(axis=0)
+            mn[p] = np.asarray(seg.min(axis=0), dtype=np.float64)
+            mx[p] = np.asarray(seg.max(axis=0), dtype=np.float64)
         kmins.append(mn)
         kmaxs.append(mx)
     return kmins, kmaxs

@@ -1,0 +1,149 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every function
+include/flashblock.h declares, sizes its workspace from the shape alone, and rejects bad
+arguments with the documented status before anything is enqueued."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import cached_kv_prefix_amd as fb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "flashblock.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:fb|losa)_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = fb.load()
+    names = header_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(fb.EXPORTS)
+
+
+def test_status_strings():
+    lib = fb.load()
+    assert lib.fb_status_string(0) == b"ok"
+    assert lib.fb_status_string(3) == b"workspace too small"
+    assert lib.fb_status_string(99) == b"unknown status"
+
+
+def dllm_shape(**kw):
+    base = dict(batch=1, h_q=32, h_kv=32, head_dim=128, block=32, seqlen_k=32768)
+    base.update(kw)
+    return fb.make_shape(**base)
+
+
+def test_workspace_size_depends_on_shape_only():
+    a = fb.workspace_size(dllm_shape())
+    assert a == fb.workspace_size(dllm_shape()) and a > 0
+    # 32 heads x 32 rows x 128 dims x 4 B per prefix chunk + stats; more chunks, more bytes
+    s1 = fb.workspace_size(dllm_shape(num_splits=1))
+    s32 = fb.workspace_size(dllm_shape(num_splits=32))
+    assert s1 < s32
+    assert s32 >= 32 * 32 * 32 * 128 * 4
+
+
+def test_workspace_size_zero_on_invalid_shape():
+    assert fb.workspace_size(dllm_shape(h_kv=5)) == 0
+    assert fb.workspace_size(dllm_shape(head_dim=96)) == 0
+
+
+class Fake:
+    """Stand-in for a device tensor: only a pointer value (never dereferenced on error)."""
+    def __init__(self, ptr=0x10000, n=1 << 30):
+        self.p, self.n = ptr, n
+
+    def data_ptr(self):
+        return self.p
+
+    def numel(self):
+        return self.n
+
+    def element_size(self):
+        return 1
+
+
+def call_step(shape, **over):
+    lib = fb.load()
+    args = dict(q=Fake(), k=Fake(), v=Fake(), kb=Fake(), vb=Fake(), mask=None, ca=Fake(), cl=Fake(), af=Fake(),
+                lf=None, ws=Fake(), ws_bytes=1 << 40)
+    args.update(over)
+    p = lambda t: None if t is None else C.c_void_p(t.data_ptr())
+    return lib.fb_step(C.byref(shape), p(args["q"]), p(args["k"]), p(args["v"]), p(args["kb"]), p(args["vb"]),
+                       p(args["mask"]), p(args["ca"]), p(args["cl"]), p(args["af"]), p(args["lf"]), p(args["ws"]),
+                       args["ws_bytes"], None, None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(kb=None), 1), (dict(ca=None), 1), (dict(af=None), 1),
+    (dict(q=Fake(0x10004)), 1),                  # misaligned
+    (dict(ws_bytes=16), 3), (dict(ws=None), 3),
+])
+def test_step_rejects_bad_pointers(over, code):
+    assert call_step(dllm_shape(), **over) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(h_kv=3), 1), (dict(batch=0), 1), (dict(block=0), 1), (dict(head_dim=96), 2),
+    (dict(flags=1), 1), (dict(num_splits=-1), 1), (dict(seqlen_k=-5), 1), (dict(softmax_scale=-1.0), 1),
+    (dict(softmax_scale=float("inf")), 1), (dict(dtype=7), 1), (dict(dtype=fb.FB_F32, head_dim=512), 2),
+])
+def test_step_rejects_bad_shapes(kw, code):
+    assert call_step(dllm_shape(**kw)) == code
+
+
+def test_prefix_rejects_bad_args_before_launch():
+    lib = fb.load()
+    s = dllm_shape()
+    r = lib.fb_prefix_attn(C.byref(s), C.c_void_p(0x10000), None, None, C.c_void_p(0x10000), C.c_void_p(0x10000),
+                           C.c_void_p(0x10000), 1 << 40, None)
+    assert r == 1
+
+
+def test_lse_merge_validation():
+    lib = fb.load()
+    assert lib.fb_lse_merge(-1, 128, None, None, None, None, None, 0, None, None) == 1
+    assert lib.fb_lse_merge(0, 128, None, None, None, None, None, 0, None, None) == 0   # nothing to do
+    assert lib.fb_lse_merge(4, 0, None, None, None, None, None, 0, None, None) == 1
+    assert lib.fb_lse_merge(4, 512, None, None, None, None, None, 0, None, None) == 2
+    assert lib.fb_lse_merge(4, 128, None, None, None, None, None, 0, None, None) == 1
+
+
+def losa_shape(**kw):
+    s = dllm_shape(block=64, seqlen_k=131072)
+    base = dict(page_size=16, topk=64, n_active=8)
+    base.update(kw)
+    return fb.make_losa_shape(s, **base)
+
+
+def test_losa_sizes():
+    ls = losa_shape()
+    assert ls.max_pages == 8192
+    assert fb.losa_meta_bytes(ls) == 32 * 128 * 8192 * 2          # 64 MiB each for kmin / kmax
+    assert fb.losa_union_capacity(ls) == 8 * 64                   # |A| * G * topk
+    assert fb.losa_workspace_size(ls) >= 32 * 8 * 8192 * 8        # fp64 page scores
+    assert fb.losa_workspace_size(losa_shape(n_active=65)) == 0   # |A| > B
+    assert fb.losa_workspace_size(fb.make_losa_shape(dllm_shape(block=64, seqlen_k=131072), max_pages=100)) == 0
+
+
+def test_losa_select_rejects_small_workspace():
+    lib = fb.load()
+    ls = losa_shape()
+    f = C.c_void_p(0x10000)
+    r = lib.losa_select_union(C.byref(ls), f, f, f, f, f, f, f, f, f, 64, None)
+    assert r == 3
+
+
+def test_mask_validation():
+    lib = fb.load()
+    assert lib.fb_mask_threshold(None, 4, 1, 32, None, None) == 1
+    assert lib.fb_mask_similarity(None, 0.95, 0, None, None) == 0
+    assert lib.fb_mask_similarity(None, 0.95, 4, None, None) == 1
+    assert lib.fb_head_cosine(0, 32, 32, 128, None, None, None, None) == 1
