@@ -1,0 +1,356 @@
+"""Benchmark of the FlashBlock step on one MI355X.
+
+Headline workload: dLLM-like step, batch 1, 32 heads (MHA), head_dim 128, block B = 32,
+prefix 32768 tokens, bf16, Q/K/V ~ N(0,1)/sqrt(128).  One step = the reuse decision
+(threshold rule on the drawn updated-token count) + fb_step (split-KV prefix pass, block
+pass, chunk reduction, cache write and log-space merge).  The timed step is a fresh
+(recompute) step: every prefix token is read.
+
+Prints ONE JSON line.  `value` is the K/V bytes of the prefix read per second of step
+time (inputs resident in HBM).  `roofline` is the attention kernel's algorithmic bytes
+over its own average duration (HIP events recorded by the library on its stream around
+that kernel).  `cpu_baseline` is the fp64 oracle timed on the host cores on a bounded
+sample of the same step.  `extra` holds the reuse step, an 8-step block, and the other
+workloads (ragged GQA, video block, LoSA sparse step).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+COUNTERS = os.path.join(ROOT, "profiles", "attn_bf16_dllm_pmc.txt")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only-main", action="store_true", help="headline workload only (for profiling)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one device copy of this many MiB first (counter calibration)")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """HIP events created through the runtime, so that events the library records on its
+    stream can be read back (torch.cuda.Event only tracks its own record() calls)."""
+    def __init__(self, n):
+        import ctypes as C
+        self.C = C
+        self.rt = C.CDLL("libamdhip64.so")
+        self.rt.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [C.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            pair = []
+            for _ in range(2):
+                e = C.c_void_p()
+                assert self.rt.hipEventCreate(C.byref(e)) == 0
+                pair.append(e)
+            self.ev.append(tuple(pair))
+
+    def ms(self):
+        out = []
+        for a, b in self.ev:
+            x = self.C.c_float()
+            assert self.rt.hipEventElapsedTime(self.C.byref(x), a, b) == 0
+            out.append(x.value)
+        return out
+
+    def close(self):
+        for a, b in self.ev:
+            self.rt.hipEventDestroy(a)
+            self.rt.hipEventDestroy(b)
+
+
+def setup_step(fb, p, dev, varlen=False):
+    import torch
+    shape = (fb.make_shape(p.batch, p.h_q, p.h_kv, p.d, p.B, cu_seqlens_k=dev["cu"], max_seqlen_k=int(p.seqlens.max()))
+             if varlen else fb.make_shape(p.batch, p.h_q, p.h_kv, p.d, p.B, seqlen_k=int(p.seqlens[0])))
+    b, B, h, d = p.q.shape
+    bufs = dict(
+        ws=torch.empty(fb.workspace_size(shape), dtype=torch.uint8, device="cuda"),
+        ca=torch.zeros((b, B, h, d), device="cuda"), cl=torch.zeros((b, B, h), device="cuda"),
+        af=torch.zeros((b, B, h, d), dtype=torch.bfloat16, device="cuda"), lf=torch.zeros((b, B, h), device="cuda"),
+        mask=torch.zeros((b, h), dtype=torch.uint8, device="cuda"),
+    )
+    return shape, bufs
+
+
+def run_step(fb, shape, dev, bufs, mask_src=None, tau=4, trace=None, sim=None, gamma=0.95):
+    """One step: the threshold rule (updated-token count per sequence, evaluated inside the
+    step) or the similarity rule (per-head mask, then the step); no rule = recompute all."""
+    if mask_src is not None:
+        fb.step_threshold(shape, dev["q"], dev["k"], dev["v"], dev["k_blk"], dev["v_blk"], mask_src, tau,
+                          bufs["ca"], bufs["cl"], bufs["af"], bufs["lf"], bufs["ws"], trace=trace)
+        return
+    if sim is not None:
+        fb.mask_similarity(sim, gamma, bufs["mask"])
+    fb.step(shape, dev["q"], dev["k"], dev["v"], dev["k_blk"], dev["v_blk"], bufs["mask"], bufs["ca"], bufs["cl"],
+            bufs["af"], bufs["lf"], bufs["ws"], trace=trace)
+
+
+def time_steps(fn, steps, warmup):
+    """Warm up, then time `steps` calls back to back (synchronised on both sides); the
+    library records a HIP event pair around the attention kernel of every call."""
+    import torch
+    import cached_kv_prefix_amd as fb
+    for _ in range(warmup):
+        fn(None)
+    torch.cuda.synchronize()
+    ev = HipEvents(steps)
+    tr = []
+    for a, b in ev.ev:
+        t = fb.FbTrace()
+        t.attn_begin, t.attn_end = a.value, b.value
+        tr.append(t)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(tr[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    kern = ev.ms()
+    ev.close()
+    return wall, float(np.mean(kern)) / 1e3, kern
+
+
+def flushed_step_times(fn, n=10):
+    """Per-step event timing with a 1 GiB scratch write before each step (outside the
+    events), so the 256 MB last-level cache holds none of the inputs."""
+    import torch
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    out = []
+    for _ in range(n):
+        scratch.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn(None)
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) / 1e3)
+    del scratch
+    return float(np.median(out))
+
+
+STREAM_KERNEL = "fb::attn_stream_kernel<1, 40, false>"
+
+
+def kernel_source_sha():
+    """Fingerprint of every kernel and host source the attention launch depends on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "cached_kv_prefix_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()
+
+
+def counters_for(src_sha):
+    """HBM traffic of the attention kernel from the committed rocprofv3 --pmc summary, if
+    it was taken on the current kernel source."""
+    if not os.path.exists(COUNTERS):
+        return None
+    kv = {}
+    for line in open(COUNTERS):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != src_sha:
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(p):
+    """The oracle (numpy fp64, as it stands) on a bounded sample of the headline step:
+    the full prefix pass of a few heads plus their block pass and merge."""
+    from oracle.attention import attend, lse_merge
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    heads = [0, 1, 2, 3]
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        for h in heads:
+            ao, lo = attend(p.q[0, :, h], p.k[:, h], p.v[:, h], p.scale)
+            ai, li = attend(p.q[0, :, h], p.k_blk[0, :, h], p.v_blk[0, :, h], p.scale)
+            lse_merge(ao, lo, ai, li)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > 10.0 or reps >= 20:
+            break
+    per_head = el / (reps * len(heads))
+    step_s = per_head * p.h_q
+    kv_bytes = p.k.shape[0] * p.h_kv * p.d * 2 * 2
+    return dict(value=kv_bytes / step_s / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
+                sample=f"{len(heads)} of {p.h_q} heads x {reps} reps (full 32768-token prefix + block + merge per "
+                       f"head), scaled to the 32-head step: {step_s * 1e3:.1f} ms per step",
+                step_ms=step_s * 1e3)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    import cached_kv_prefix_amd as fb
+    import synth
+    from synth.device import to_device, tensor
+    fb.load()
+    torch.cuda.init()
+
+    if args.copy_probe_mib > 0:
+        src = torch.ones(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---------------------------------------------------------------- headline workload
+    p = synth.dllm()
+    dev = to_device(p)
+    shape, bufs = setup_step(fb, p, dev)
+    m_all = torch.from_numpy(p.extra["m_updated"]).cuda()       # [8 steps, batch]
+    m_fresh = m_all[0]                                           # step 0: recompute
+    wall, attn_s, _ = time_steps(lambda tr: run_step(fb, shape, dev, bufs, m_fresh, trace=tr),
+                                 args.steps, args.warmup)
+    kv_bytes = p.k.shape[0] * p.h_kv * p.d * 2 * 2               # K and V of the prefix
+    attn_bytes = kv_bytes + p.q.size * 2 + p.k_blk.size * 2 * 2  # + Q + block K/V
+    value = kv_bytes / wall / 1e9
+    src_sha = kernel_source_sha()
+    traffic = counters_for(src_sha)
+    achieved = attn_bytes / attn_s / 1e9
+
+    extra = {"step_us": wall * 1e6, "attn_kernel_us": attn_s * 1e6, "tokens_per_s": p.B / wall,
+             "kv_bytes": kv_bytes, "attn_kernel_alg_bytes": attn_bytes,
+             "step_frac_of_hbm_peak": value / HBM_PEAK_GBS}
+    if not args.only_main:
+        # reuse step: every head reuses, only the block pass and the merge run
+        one = torch.zeros_like(m_fresh)
+        wall_r, _, _ = time_steps(lambda tr: run_step(fb, shape, dev, bufs, one, trace=tr), args.steps, 3)
+        extra["reuse_step_us"] = wall_r * 1e6
+        # an 8-step block with the drawn M (tau 4): mean step time
+        def block(tr):
+            for s in range(8):
+                run_step(fb, shape, dev, bufs, m_all[s], trace=tr)
+        wall_b, _, _ = time_steps(block, max(5, args.steps // 8), 2)
+        fresh = int(1 + (p.extra["m_updated"][1:, 0] >= 4).sum())
+        extra["block8_mean_step_us"] = wall_b / 8 * 1e6
+        extra["block8_fresh_steps"] = fresh
+        extra["cold_fresh_step_us"] = flushed_step_times(lambda tr: run_step(fb, shape, dev, bufs, m_fresh)) * 1e6
+        extra["workloads"] = other_workloads(fb, args)
+    result = {
+        "metric": "attn step µs & KV GB/s (B=32, 32k prefix, bf16); % of HBM/MFMA peak",
+        "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "dLLM fresh step: batch 1, 32 heads MHA, head_dim 128, block 32, prefix 32768, bf16, "
+                               "Q/K/V ~ N(0,1)/sqrt(128)", "global_batch": 1, "seq_len": 32768, "block": 32,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": STREAM_KERNEL + " (split-KV prefix + block pass, one launch)"},
+        "extra": extra,
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(p)
+    print(json.dumps(result))
+
+
+def other_workloads(fb, args):
+    import torch
+    import synth
+    from synth.device import to_device, tensor
+    out = {}
+    steps = max(5, args.steps // 5)
+    # ragged GQA: per-sequence threshold mask from the drawn M
+    p = synth.ragged()
+    dev = to_device(p)
+    shape, bufs = setup_step(fb, p, dev, varlen=True)
+    fresh = torch.full((p.batch,), 1 << 30, dtype=torch.int32, device="cuda")
+    w_f, a_f, _ = time_steps(lambda tr: run_step(fb, shape, dev, bufs, fresh, trace=tr), steps, 3)
+    m = torch.from_numpy(p.extra["m_updated"]).cuda()
+    w_m, _, _ = time_steps(lambda tr: run_step(fb, shape, dev, bufs, m, trace=tr), steps, 3)
+    kv = int(p.seqlens.sum()) * p.h_kv * p.d * 4
+    fresh_frac = float((p.extra["m_updated"] >= 4).mean())
+    out["ragged_gqa"] = {"fresh_step_us": w_f * 1e6, "attn_kernel_us": a_f * 1e6, "kv_GBps": kv / w_f / 1e9,
+                         "frac_hbm": kv / a_f / 1e9 / HBM_PEAK_GBS, "masked_step_us": w_m * 1e6,
+                         "fresh_sequences": fresh_frac, "total_prefix_tokens": int(p.seqlens.sum())}
+    del dev, bufs
+    # video block: per-head similarity mask, 7 of 12 heads reuse
+    p = synth.video()
+    dev = to_device(p)
+    shape, bufs = setup_step(fb, p, dev)
+    sim = torch.from_numpy(p.extra["sim"]).cuda()
+    w_all, a_all, _ = time_steps(lambda tr: run_step(fb, shape, dev, bufs, None, trace=tr), steps, 2)
+    w_m, a_m, _ = time_steps(lambda tr: run_step(fb, shape, dev, bufs, None, sim=sim, trace=tr), steps, 2)
+    nq, nb, npre, d = p.B, p.B, int(p.seqlens[0]), p.d
+    flop_block = 4.0 * nq * nb * d * p.h_q
+    flop_pre = 4.0 * nq * npre * d
+    n_fresh = int((p.extra["sim"] <= np.float32(p.extra["gamma"])).sum())
+    f_masked = flop_block + n_fresh * flop_pre
+    f_all = flop_block + p.h_q * flop_pre
+    out["video_block"] = {"masked_step_us": w_m * 1e6, "masked_TFLOPs": f_masked / w_m / 1e12,
+                          "masked_frac_mfma": f_masked / w_m / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                          "all_fresh_step_us": w_all * 1e6, "all_fresh_TFLOPs": f_all / w_all / 1e12,
+                          "attn_kernel_all_fresh_frac_mfma": f_all / a_all / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                          "fresh_heads": n_fresh, "tokens_per_s": nq / w_m}
+    del dev, bufs
+    # LoSA sparse step
+    p = synth.losa()
+    dev = to_device(p)
+    shape, bufs = setup_step(fb, p, dev)
+    ls = fb.make_losa_shape(shape, page_size=16, topk=64, n_active=8)
+    el = 2
+    kmin = torch.empty(fb.losa_meta_bytes(ls) // el, dtype=torch.bfloat16, device="cuda")
+    kmax = torch.empty_like(kmin)
+    fb.losa_page_meta(ls, dev["k"], kmin, kmax)
+    qc, qp = tensor(p.extra["q_cur"]), tensor(p.extra["q_prev"])
+    cap = fb.losa_union_capacity(ls)
+    sel = dict(active=torch.empty((1, 8), dtype=torch.int32, device="cuda"),
+               topk=torch.empty((1, 32, 8, 64), dtype=torch.int32, device="cuda"),
+               union=torch.empty((1, 32, cap), dtype=torch.int32, device="cuda"),
+               count=torch.empty((1, 32), dtype=torch.int32, device="cuda"),
+               ws=torch.empty(fb.losa_workspace_size(ls), dtype=torch.uint8, device="cuda"))
+    fresh = torch.full((1,), 1 << 30, dtype=torch.int32, device="cuda")
+    w_d, _, _ = time_steps(lambda tr: run_step(fb, shape, dev, bufs, fresh, trace=tr), steps, 2)
+
+    def sparse(tr):
+        fb.losa_step(ls, qc, qp, dev["k"], dev["v"], dev["k_blk"], dev["v_blk"], kmin, kmax, bufs["ca"], bufs["cl"],
+                     bufs["af"], bufs["lf"], sel["active"], sel["topk"], sel["union"], sel["count"], sel["ws"],
+                     trace=tr)
+    w_s, a_s, _ = time_steps(sparse, steps, 2)
+    cnt = sel["count"].cpu().numpy()
+    union_bytes = float(cnt.sum()) * 16 * p.d * 2 * 2
+    meta_bytes = 2 * fb.losa_meta_bytes(ls)
+    out["losa_sparse"] = {"sparse_step_us": w_s * 1e6, "attn_kernel_us": a_s * 1e6, "dense_step_us": w_d * 1e6,
+                          "union_pages_mean": float(cnt.mean()), "density": float(cnt.mean()) / ls.max_pages,
+                          "alg_bytes": meta_bytes + union_bytes,
+                          "frac_hbm_step": (meta_bytes + union_bytes) / w_s / 1e9 / HBM_PEAK_GBS}
+    return out
+
+
+if __name__ == "__main__":
+    main()

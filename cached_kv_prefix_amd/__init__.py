@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libflashblock.so")
 FB_BF16, FB_F32 = 0, 1
 STATUS = {0: "FB_OK", 1: "FB_ERR_INVALID_ARG", 2: "FB_ERR_UNSUPPORTED", 3: "FB_ERR_WORKSPACE", 5: "FB_ERR_HIP"}
 EXPORTS = ("fb_status_string", "fb_workspace_size", "fb_prefix_attn", "fb_block_attn", "fb_lse_merge",
-           "fb_step", "fb_mask_threshold", "fb_mask_similarity", "fb_head_cosine", "losa_meta_bytes",
+           "fb_step", "fb_step_threshold", "fb_mask_threshold", "fb_mask_similarity", "fb_head_cosine", "losa_meta_bytes",
            "losa_workspace_size", "losa_union_capacity", "losa_page_meta", "losa_select_union", "losa_step")
 
 
@@ -64,6 +64,7 @@ def load(path: str | None = None):
         "fb_block_attn": (i32, [sp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "fb_lse_merge": (i32, [i64, i32, vp, vp, vp, vp, vp, i32, vp, vp]),
         "fb_step": (i32, [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, tp, vp]),
+        "fb_step_threshold": (i32, [sp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, tp, vp]),
         "fb_mask_threshold": (i32, [vp, i32, i32, i32, vp, vp]),
         "fb_mask_similarity": (i32, [vp, f32, i64, vp, vp]),
         "fb_head_cosine": (i32, [i32, i32, i32, i32, vp, vp, vp, vp]),
@@ -160,6 +161,15 @@ def step(shape, q, k, v, k_blk, v_blk, reuse_mask, cache_a, cache_l, a_full, l_f
                           _ptr(cache_a), _ptr(cache_l), _ptr(a_full), _ptr(l_full), _ptr(ws),
                           0 if ws is None else ws.numel() * ws.element_size(),
                           None if trace is None else C.byref(trace), _stream(stream)), "fb_step")
+
+
+def step_threshold(shape, q, k, v, k_blk, v_blk, m_updated, tau, cache_a, cache_l, a_full, l_full, ws,
+                   trace=None, stream=None):
+    _check(load().fb_step_threshold(C.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(k_blk), _ptr(v_blk),
+                                    _ptr(m_updated), tau, _ptr(cache_a), _ptr(cache_l), _ptr(a_full),
+                                    _ptr(l_full), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                    None if trace is None else C.byref(trace), _stream(stream)),
+           "fb_step_threshold")
 
 
 def mask_threshold(m_updated, tau, h_q, mask, stream=None):

@@ -1,5 +1,6 @@
 // Host side of the C ABI declared in include/flashblock.h: argument validation (before
 // anything is enqueued), the shape-only split plan, workspace carving and launches.
+#include <algorithm>
 #include <math.h>
 #include <string.h>
 
@@ -10,9 +11,18 @@ using namespace fb;
 
 namespace {
 
-constexpr int kTileKeys = 128;       // key tile of the bf16 attention kernel
-constexpr int kTargetItems = 1024;   // workgroups the split plan aims for (256 CUs x 4)
-constexpr int kMinChunk = 512;       // smallest automatic chunk (keys)
+#ifndef FB_TARGET_ITEMS
+#define FB_TARGET_ITEMS 1024
+#endif
+#ifndef FB_STREAM_TARGET_ITEMS
+#define FB_STREAM_TARGET_ITEMS 256   // the streaming kernel runs one workgroup per CU
+#endif
+#ifndef FB_MIN_CHUNK
+#define FB_MIN_CHUNK 512
+#endif
+constexpr int kTileKeys = 128;                 // chunks are whole 128-key tiles
+constexpr int kTargetItems = FB_TARGET_ITEMS;  // workgroups the split plan aims for
+constexpr int kMinChunk = FB_MIN_CHUNK;        // smallest automatic chunk (keys)
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -66,7 +76,14 @@ RowPlan row_plan(const fb_shape* s, int rows_per_head) {
 struct SplitPlan {
   int chunk, splits;
 };
-SplitPlan split_plan(const fb_shape* s, const RowPlan& rp, int64_t max_keys, int forced) {
+// `reserved` work items of the same launch (the block pass) come out of the streaming
+// kernel's budget, so that the whole launch is resident at once: the block items are the
+// last to be dispatched, and waiting for a free CU they would add their whole latency to
+// the end of the launch.
+bool stream_rows(const fb_shape* s, const RowPlan& rp) {
+  return s->dtype == FB_BF16 && s->head_dim == 128 && rp.rows <= 32;
+}
+SplitPlan split_plan(const fb_shape* s, const RowPlan& rp, int64_t max_keys, int forced, int64_t reserved = 0) {
   SplitPlan p;
   if (max_keys <= 0) {
     p.chunk = kTileKeys;
@@ -78,10 +95,13 @@ SplitPlan split_plan(const fb_shape* s, const RowPlan& rp, int64_t max_keys, int
     want = forced;
   } else {
     const int64_t items = (int64_t)s->batch * s->h_kv * rp.qgroups;
-    want = cdiv(kTargetItems, items);
+    want = stream_rows(s, rp) ? std::max<int64_t>(1, (FB_STREAM_TARGET_ITEMS - reserved) / items)
+                              : cdiv(kTargetItems, items);
   }
   int64_t chunk = round_up(cdiv(max_keys, want), kTileKeys);
   if (forced <= 0 && chunk < kMinChunk) chunk = kMinChunk < round_up(max_keys, kTileKeys) ? kMinChunk : round_up(max_keys, kTileKeys);
+  // a streaming work item walks at most 128 * kStreamTmax keys (longer prefixes take more items)
+  if (forced <= 0 && stream_rows(s, rp)) chunk = std::min<int64_t>(chunk, 128 * kStreamTmax);
   p.chunk = (int)chunk;
   p.splits = (int)cdiv(max_keys, chunk);
   return p;
@@ -109,8 +129,9 @@ struct StepPlan {
 StepPlan step_plan(const fb_shape* s) {
   StepPlan p;
   p.rp = row_plan(s, s->block);
-  p.pre = split_plan(s, p.rp, max_prefix(s), s->num_splits);
   p.blk = split_plan(s, p.rp, s->block, 0);
+  const int64_t blk_items = (int64_t)s->batch * s->h_kv * p.rp.qgroups * p.blk.splits;
+  p.pre = split_plan(s, p.rp, max_prefix(s), s->num_splits, blk_items);
   p.rpre = partial_region(s, p.rp, p.pre, 0);
   p.rblk = partial_region(s, p.rp, p.blk, p.rpre.bytes);
   p.ws_bytes = p.rpre.bytes + p.rblk.bytes;
@@ -146,6 +167,7 @@ AttnArgs base_args(const fb_shape* s, const void* q) {
   a.h_kv = s->h_kv;
   a.G = s->h_q / s->h_kv;
   a.d = s->head_dim;
+  a.max_seqlen = max_prefix(s);
   a.scale_log2 = scale_of(s) * 1.4426950408889634f;
   return a;
 }
@@ -254,9 +276,11 @@ fb_status fb_lse_merge(int64_t rows, int32_t d, const float* a_out, const float*
   return hip_status(launch_lse_merge(rows, d, a_out, l_out, a_in, l_in, a_full, out_dtype == FB_BF16, l_full, stream));
 }
 
-fb_status fb_step(const fb_shape* s, const void* q, const void* k, const void* v, const void* k_blk,
-                  const void* v_blk, const uint8_t* reuse_mask, float* cache_a, float* cache_l, void* a_full,
-                  float* l_full, void* ws, size_t ws_bytes, const fb_trace* trace, hipStream_t stream) {
+namespace {
+fb_status run_step(const fb_shape* s, const void* q, const void* k, const void* v, const void* k_blk,
+                   const void* v_blk, const uint8_t* reuse_mask, const int32_t* m_upd, int32_t tau,
+                   float* cache_a, float* cache_l, void* a_full, float* l_full, void* ws, size_t ws_bytes,
+                   const fb_trace* trace, hipStream_t stream) {
   fb_status st = check_shape(s);
   if (st != FB_OK) return st;
   if ((st = check_inputs(s, q, k, v)) != FB_OK) return st;
@@ -267,6 +291,8 @@ fb_status fb_step(const fb_shape* s, const void* q, const void* k, const void* v
   AttnArgs a = base_args(s, q);
   a.src0 = make_src(p.rp, p.pre, k, v, s->cu_seqlens_k, s->seqlen_k, (float*)ws, p.rpre);
   a.src0.mask = reuse_mask;
+  a.src0.m_upd = m_upd;
+  a.src0.tau = tau;
   a.src1 = make_src(p.rp, p.blk, k_blk, v_blk, nullptr, s->block, (float*)ws, p.rblk);
   rec(trace ? trace->attn_begin : nullptr, stream);
   if (hipError_t e = launch_attn(a, s->dtype == FB_BF16, stream)) return hip_status(e);
@@ -274,6 +300,8 @@ fb_status fb_step(const fb_shape* s, const void* q, const void* k, const void* v
   CombineArgs c = base_combine(s, p, (float*)ws);
   c.mode = kModeStep;
   c.mask = reuse_mask;
+  c.m_upd = m_upd;
+  c.tau = tau;
   c.cache_a = cache_a;
   c.cache_l = cache_l;
   c.a_full = a_full;
@@ -282,6 +310,23 @@ fb_status fb_step(const fb_shape* s, const void* q, const void* k, const void* v
   if (hipError_t e = launch_combine(c, stream)) return hip_status(e);
   rec(trace ? trace->merge_end : nullptr, stream);
   return FB_OK;
+}
+}  // namespace
+
+fb_status fb_step(const fb_shape* s, const void* q, const void* k, const void* v, const void* k_blk,
+                  const void* v_blk, const uint8_t* reuse_mask, float* cache_a, float* cache_l, void* a_full,
+                  float* l_full, void* ws, size_t ws_bytes, const fb_trace* trace, hipStream_t stream) {
+  return run_step(s, q, k, v, k_blk, v_blk, reuse_mask, nullptr, 0, cache_a, cache_l, a_full, l_full, ws,
+                  ws_bytes, trace, stream);
+}
+
+fb_status fb_step_threshold(const fb_shape* s, const void* q, const void* k, const void* v, const void* k_blk,
+                            const void* v_blk, const int32_t* m_updated, int32_t tau, float* cache_a,
+                            float* cache_l, void* a_full, float* l_full, void* ws, size_t ws_bytes,
+                            const fb_trace* trace, hipStream_t stream) {
+  if (!m_updated) return FB_ERR_INVALID_ARG;
+  return run_step(s, q, k, v, k_blk, v_blk, nullptr, m_updated, tau, cache_a, cache_l, a_full, l_full, ws,
+                  ws_bytes, trace, stream);
 }
 
 fb_status fb_mask_threshold(const int32_t* m_updated, int32_t tau, int32_t batch, int32_t h_q, uint8_t* mask,

@@ -13,59 +13,24 @@
 //   * keys stream through LDS in 128-key tiles (K and V rows padded to 2d+16 bytes); every
 //     thread keeps the next tile's 16-byte chunks in registers while the waves compute on
 //     the current tile, so HBM loads overlap the MFMA work;
-//   * a wave owns 32 query rows; with 32 rows per group the 4 waves split each tile's keys
-//     (32 keys each), with 64 rows 2 waves share a query tile, with >= 128 rows each wave
-//     has its own query tile and all 128 keys;
+//   * a wave owns 32 query rows; the waves that share a query tile (4 with 32 rows per
+//     group, 2 with 64, 1 with >= 128) take the chunk's 32-key sub-tiles round-robin;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys x queries), so a lane holds one query
 //     and 16 keys: the row max needs one cross-half exchange; P stays in registers and is
 //     the B operand of O^T = V^T P^T, whose A operand reads V columns from LDS;
 //   * the waves that share query rows are combined through LDS before one partial per
 //     row is written.
-#include "fb_device.hpp"
-#include "fb_internal.hpp"
+#include "fb_attn_common.hpp"
 
 namespace fb {
 
 namespace {
 
-struct SeqInfo {
-  int seq0, n_seq, n_keys;
-};
-
-__device__ __forceinline__ SeqInfo seq_info(const AttnSrc& S, int b, int hk, int h_kv) {
-  SeqInfo r;
-  if (S.cu) {
-    r.seq0 = S.cu[b];
-    r.n_seq = S.cu[b + 1] - r.seq0;
-  } else {
-    r.seq0 = b * S.n_uniform;
-    r.n_seq = S.n_uniform;
-  }
-  r.n_keys = S.pages ? S.page_count[b * h_kv + hk] * S.page_size : r.n_seq;
-  return r;
-}
-
-// Token (within the sequence) of source key `key`; clamps to a readable token and
-// reports whether the key takes part in the softmax.
-__device__ __forceinline__ int key_token(const AttnSrc& S, const int32_t* pg, int key,
-                                         int kend, int n_seq, bool& ok) {
-  ok = key < kend;
-  if (!ok) key = kend - 1;
-  if (pg) {
-    int t = pg[key / S.page_size] * S.page_size + key % S.page_size;
-    if (t >= n_seq) {
-      ok = false;
-      t = n_seq - 1;
-    }
-    return t;
-  }
-  return key;
-}
-
 // True when this item has work: the chunk is inside the key range and (with a reuse
 // mask) at least one query head covered by the workgroup recomputes.
 __device__ __forceinline__ bool item_live(const AttnArgs& A, const AttnSrc& S, int b, int hk,
                                           int wg_row0, int wg_rows) {
+  if (S.m_upd) return S.m_upd[b] >= S.tau;
   if (!S.mask) return true;
   const int j0 = wg_row0 / S.rows_per_head;
   const int j1 = (wg_row0 + wg_rows - 1) / S.rows_per_head;
@@ -76,9 +41,34 @@ __device__ __forceinline__ bool item_live(const AttnArgs& A, const AttnSrc& S, i
 
 }  // namespace
 
+#ifndef FB_ATTN_KT
+#define FB_ATTN_KT 128                 // keys per LDS tile
+#endif
+#ifndef FB_ATTN_OCC
+#define FB_ATTN_OCC 2                  // workgroups per CU the register budget targets
+#endif
+#ifndef FB_GRID_HEAD_MAJOR
+#define FB_GRID_HEAD_MAJOR 1           // consecutive workgroups take consecutive heads
+#endif
+
+// Work item of a workgroup: (source split, KV head x query group, sequence).  With the
+// head-major order, workgroups resident at the same time spread over all KV heads, whose
+// rows interleave in memory, instead of walking one head's rows.
+struct Item {
+  int x, y;
+};
+__device__ __forceinline__ Item item_of(int heads_groups) {
+#if FB_GRID_HEAD_MAJOR
+  return Item{(int)blockIdx.y, (int)blockIdx.x};
+#else
+  (void)heads_groups;
+  return Item{(int)blockIdx.x, (int)blockIdx.y};
+#endif
+}
+
 template <int D>
-__global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs A) {
-  constexpr int KT = 128;              // keys per LDS tile
+__global__ void __launch_bounds__(256, FB_ATTN_OCC) attn_bf16_kernel(const AttnArgs A) {
+  constexpr int KT = FB_ATTN_KT;       // keys per LDS tile
   constexpr int ROWB = 2 * D + 16;     // padded LDS row (bytes)
   constexpr int CPR = (2 * D) / 16;    // 16-byte chunks per key row
   constexpr int KPP = 256 / CPR;       // key rows covered by one pass of the workgroup
@@ -92,12 +82,13 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs A) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, ql = lane & 31;
-  const bool second = blockIdx.x >= (unsigned)A.src0.n_splits;
+  const Item it = item_of(0);
+  const bool second = it.x >= A.src0.n_splits;
   const AttnSrc& S = second ? A.src1 : A.src0;
-  const int split = second ? blockIdx.x - A.src0.n_splits : blockIdx.x;
+  const int split = second ? it.x - A.src0.n_splits : it.x;
   const int b = blockIdx.z;
-  const int hk = blockIdx.y % A.h_kv;
-  const int qg = blockIdx.y / A.h_kv;
+  const int hk = it.y % A.h_kv;
+  const int qg = it.y / A.h_kv;
   if (qg >= S.qgroups) return;
   const SeqInfo si = seq_info(S, b, hk, A.h_kv);
   const int kbeg = split * S.chunk;
@@ -165,8 +156,10 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs A) {
     __syncthreads();
     if (t + 1 < ntiles) FB_LOAD_TILE(kbeg + (t + 1) * KT);
     if (!wave_active) continue;
-    for (int st = 0; st < tq; ++st) {
-      const int kb = slice * (KT / ks) + st * 32;
+    for (int st = 0; st < KT / 32; ++st) {
+      // 32-key sub-tiles of the chunk are dealt round-robin to the ks waves of a query tile
+      if ((t * (KT / 32) + st) % ks != slice) continue;
+      const int kb = st * 32;
       if (kbeg + t * KT + kb >= kend) break;
       f32x16 acc = f32x16{};
       const unsigned char* kr = smem + (kb + ql) * ROWB + 16 * g;
@@ -276,12 +269,13 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const AttnArgs A) {
 // key is a butterfly sum (identical on every lane), then the same online update.
 __global__ void __launch_bounds__(256) attn_f32_kernel(const AttnArgs A) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const bool second = blockIdx.x >= (unsigned)A.src0.n_splits;
+  const Item it = item_of(0);
+  const bool second = it.x >= A.src0.n_splits;
   const AttnSrc& S = second ? A.src1 : A.src0;
-  const int split = second ? blockIdx.x - A.src0.n_splits : blockIdx.x;
+  const int split = second ? it.x - A.src0.n_splits : it.x;
   const int b = blockIdx.z;
-  const int hk = blockIdx.y % A.h_kv;
-  const int qg = blockIdx.y / A.h_kv;
+  const int hk = it.y % A.h_kv;
+  const int qg = it.y / A.h_kv;
   if (qg >= S.qgroups) return;
   const SeqInfo si = seq_info(S, b, hk, A.h_kv);
   const int kbeg = split * S.chunk;
@@ -349,11 +343,16 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(const AttnArgs A) {
   }
 }
 
-hipError_t launch_attn(const AttnArgs& a, bool bf16, hipStream_t st) {
+namespace {
+hipError_t launch_generic(const AttnArgs& a, bool bf16, hipStream_t st) {
   const int gx = a.src0.n_splits + a.src1.n_splits;
   const int qgroups = a.src0.qgroups > a.src1.qgroups ? a.src0.qgroups : a.src1.qgroups;
   if (gx == 0 || qgroups == 0) return hipSuccess;
+#if FB_GRID_HEAD_MAJOR
+  dim3 grid(a.h_kv * qgroups, gx, a.batch);
+#else
   dim3 grid(gx, a.h_kv * qgroups, a.batch);
+#endif
   if (bf16) {
     if (a.d == 128)
       hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(256), 0, st, a);
@@ -363,6 +362,28 @@ hipError_t launch_attn(const AttnArgs& a, bool bf16, hipStream_t st) {
     hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();
+}
+}  // namespace
+
+// bf16 groups of at most 32 rows go to the streaming kernel (fb_stream.hip), the rest to
+// the LDS-tiled kernel above.  A paged source never shares a streaming launch with the
+// block source.
+hipError_t launch_attn(const AttnArgs& a, bool bf16, hipStream_t st) {
+  if (bf16) {
+    const bool s0 = stream_ok(a, a.src0, a.max_seqlen), s1 = stream_ok(a, a.src1, a.max_seqlen);
+    const bool mixed = a.src0.pages != nullptr && a.src1.n_splits > 0;
+    if (s0 && s1 && !mixed) return launch_stream(a, st);
+    if (s0 && a.src0.n_splits > 0) {
+      AttnArgs a0 = a;
+      a0.src1.n_splits = 0;
+      if (hipError_t e = launch_stream(a0, st)) return e;
+      AttnArgs a1 = a;
+      a1.src0.n_splits = 0;
+      a1.src0.qgroups = 0;
+      return launch_generic(a1, bf16, st);
+    }
+  }
+  return launch_generic(a, bf16, st);
 }
 
 }  // namespace fb

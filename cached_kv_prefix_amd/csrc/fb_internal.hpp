@@ -29,6 +29,8 @@ struct AttnSrc {
   int32_t tq;                 // 32-row query tiles per workgroup (1, 2 or 4)
   int32_t qgroups;            // ceil(rows / (32 * tq))
   const uint8_t* mask;        // [batch][h_q]: skip a workgroup whose heads all reuse
+  const int32_t* m_upd;       // threshold rule instead of a mask: reuse where m_upd[b] < tau
+  int32_t tau;
   float* po;                  // partial O   [batch][h_kv][n_splits][rows][d]
   float* pml;                 // partial m,l [batch][h_kv][n_splits][rows][2]
 };
@@ -36,9 +38,21 @@ struct AttnSrc {
 struct AttnArgs {
   const void* q;              // [batch][B][h_q][d]
   int32_t batch, B, h_q, h_kv, G, d;
+  int32_t max_seqlen;         // longest prefix (bounds 32-bit offsets of the stream kernel)
   float scale_log2;           // softmax_scale * log2(e)
   AttnSrc src0, src1;         // grid x: [0, src0.n_splits) then [.., + src1.n_splits)
 };
+
+// Streaming kernel (fb_stream.hip): sub-tiles in flight per wave, and the most 32-key
+// sub-tiles a wave walks in one work item (its chunk is at most 4 * 32 * kStreamTmax keys).
+#ifndef FB_STREAM_DEPTH
+#define FB_STREAM_DEPTH 1
+#endif
+#ifndef FB_STREAM_TMAX
+#define FB_STREAM_TMAX 40
+#endif
+constexpr int kStreamDepth = FB_STREAM_DEPTH;
+constexpr int kStreamTmax = FB_STREAM_TMAX;
 
 enum CombineMode { kModeStep = 0, kModePrefixOnly = 1, kModeBlockOnly = 2, kModeLosa = 3 };
 
@@ -52,6 +66,7 @@ struct CombineArgs {
   // block partials (src1)
   const float* bo; const float* bml; int32_t b_rows; int32_t b_splits; int32_t b_chunk;
   const uint8_t* mask;                 // step: [batch][h_q], null = recompute all
+  const int32_t* m_upd; int32_t tau;   // step: threshold rule evaluated in place of mask
   const int32_t* active; int32_t n_active;   // LoSA
   float* cache_a; float* cache_l;      // step/LoSA cache, or prefix-only outputs
   float* ain; float* lin;              // block-only outputs
@@ -59,6 +74,8 @@ struct CombineArgs {
 };
 
 hipError_t launch_attn(const AttnArgs& a, bool bf16, hipStream_t st);
+bool stream_ok(const AttnArgs& a, const AttnSrc& s, int64_t max_tokens);
+hipError_t launch_stream(const AttnArgs& a, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& c, hipStream_t st);
 hipError_t launch_lse_merge(int64_t rows, int32_t d, const float* ao, const float* lo,
                             const float* ai, const float* li, void* af, int out_bf16,

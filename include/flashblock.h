@@ -135,6 +135,17 @@ fb_status fb_step(const fb_shape* s, const void* q, const void* k, const void* v
                   float* cache_a, float* cache_l, void* a_full, float* l_full, void* ws,
                   size_t ws_bytes, const fb_trace* trace, hipStream_t stream);
 
+/* fb_step with the threshold rule [FB-pt §2] evaluated inside the step's kernels:
+ * identical results to fb_mask_threshold(m_updated, tau) followed by fb_step with that
+ * mask, with one kernel launch fewer.  m_updated: device int32 [batch], the number of
+ * tokens updated since the previous step (the first step of a block must pass a count
+ * >= tau for every sequence). */
+fb_status fb_step_threshold(const fb_shape* s, const void* q, const void* k, const void* v,
+                            const void* k_blk, const void* v_blk, const int32_t* m_updated,
+                            int32_t tau, float* cache_a, float* cache_l, void* a_full,
+                            float* l_full, void* ws, size_t ws_bytes, const fb_trace* trace,
+                            hipStream_t stream);
+
 /* Threshold reuse rule [FB-pt §2]: mask[b][h] = (m_updated[b] < tau) for every h.
  * m_updated: device int32 [batch] (tokens updated since the previous step). */
 fb_status fb_mask_threshold(const int32_t* m_updated, int32_t tau, int32_t batch,

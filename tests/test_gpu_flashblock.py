@@ -365,3 +365,31 @@ def test_video_block_sampled(gpu_lib):
         ei, li = attend(q2[0, rows, h], p.k_blk[0, :, h], p.v_blk[0, :, h], p.scale)
         ea, _ = lse_merge(eo, lo_, ei, li)
         check_attn(af[0, rows, h], ea, "bf16", f"video head {h} reuse={em[0, h]}")
+
+
+def test_step_threshold_equals_mask_then_step(gpu_lib):
+    """fb_step_threshold (rule evaluated inside the kernels) is bitwise identical to
+    fb_mask_threshold followed by fb_step."""
+    import torch
+    fb = gpu_lib
+    p = synth.custom(8, 3, 8, 2, 128, 32, [900, 64, 2000])
+    dev = to_device(p)
+    shape = _shape(fb, p, dev, varlen=True)
+    ws = _ws(fb, shape)
+    o1, o2 = _alloc(fb, p, dev), _alloc(fb, p, dev)
+    fresh = torch.full((3,), 1 << 30, dtype=torch.int32, device="cuda")
+    for o in (o1, o2):
+        fb.step_threshold(shape, dev["q"], dev["k"], dev["v"], dev["k_blk"], dev["v_blk"], fresh, 4, o["cache_a"],
+                          o["cache_l"], o["a_full"], o["l_full"], ws)
+    m = torch.tensor([2, 7, 4], dtype=torch.int32, device="cuda")
+    q2 = tensor(synth.round_bf16(p.q * 0.5))
+    mask = torch.empty((3, 8), dtype=torch.uint8, device="cuda")
+    fb.mask_threshold(m, 4, 8, mask)
+    fb.step(shape, q2, dev["k"], dev["v"], dev["k_blk"], dev["v_blk"], mask, o1["cache_a"], o1["cache_l"],
+            o1["a_full"], o1["l_full"], ws)
+    fb.step_threshold(shape, q2, dev["k"], dev["v"], dev["k_blk"], dev["v_blk"], m, 4, o2["cache_a"], o2["cache_l"],
+                      o2["a_full"], o2["l_full"], ws)
+    torch.cuda.synchronize()
+    assert np_of(mask)[:, 0].tolist() == [1, 0, 0]
+    for k_ in ("a_full", "l_full", "cache_a", "cache_l"):
+        assert torch.equal(o1[k_], o2[k_]), k_
