@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
-COUNTERS = os.path.join(ROOT, "profiles", "attn_bf16_dllm_pmc.txt")
+COUNTERS = os.path.join(ROOT, "profiles", "attn_stream_dllm_pmc.txt")
 
 
 def parse():
