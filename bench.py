@@ -130,13 +130,15 @@ def time_steps(fn, steps, warmup):
 
 
 def flushed_step_times(fn, n=10):
-    """Per-step event timing with a 1 GiB scratch write before each step (outside the
-    events), so the 256 MB last-level cache holds none of the inputs."""
+    """Per-step event timing after a 1 GiB read before each step (outside the events), so
+    the 256 MB last-level cache holds none of the inputs.  A read, not a write: dirty
+    lines left by a write would be written back during the timed step."""
     import torch
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
     out = []
     for _ in range(n):
-        scratch.fill_(1)
+        torch.sum(scratch, dtype=torch.float32, out=sink)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         fn(None)
