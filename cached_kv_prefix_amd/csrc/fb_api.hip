@@ -83,6 +83,13 @@ struct SplitPlan {
 bool stream_rows(const fb_shape* s, const RowPlan& rp) {
   return s->dtype == FB_BF16 && s->head_dim == 128 && rp.rows <= 32;
 }
+// Large query groups run on the query-tiled kernel: 128 * kFaQt rows per work item.
+bool fa_rows(const fb_shape* s, const RowPlan& rp) {
+  return s->dtype == FB_BF16 && s->head_dim == 128 && rp.rows >= kFaMinRows;
+}
+#ifndef FB_FA_TARGET_ITEMS
+#define FB_FA_TARGET_ITEMS 512
+#endif
 SplitPlan split_plan(const fb_shape* s, const RowPlan& rp, int64_t max_keys, int forced, int64_t reserved = 0) {
   SplitPlan p;
   if (max_keys <= 0) {
@@ -95,8 +102,14 @@ SplitPlan split_plan(const fb_shape* s, const RowPlan& rp, int64_t max_keys, int
     want = forced;
   } else {
     const int64_t items = (int64_t)s->batch * s->h_kv * rp.qgroups;
-    want = stream_rows(s, rp) ? std::max<int64_t>(1, (FB_STREAM_TARGET_ITEMS - reserved) / items)
-                              : cdiv(kTargetItems, items);
+    if (stream_rows(s, rp)) {
+      want = std::max<int64_t>(1, (FB_STREAM_TARGET_ITEMS - reserved) / items);
+    } else if (fa_rows(s, rp)) {
+      const int64_t fa_items = (int64_t)s->batch * s->h_kv * cdiv(rp.rows, 32 * kFaWaves * kFaQt);
+      want = std::max<int64_t>(1, (FB_FA_TARGET_ITEMS + fa_items / 2) / fa_items);
+    } else {
+      want = cdiv(kTargetItems, items);
+    }
   }
   int64_t chunk = round_up(cdiv(max_keys, want), kTileKeys);
   if (forced <= 0 && chunk < kMinChunk) chunk = kMinChunk < round_up(max_keys, kTileKeys) ? kMinChunk : round_up(max_keys, kTileKeys);
@@ -129,7 +142,7 @@ struct StepPlan {
 StepPlan step_plan(const fb_shape* s) {
   StepPlan p;
   p.rp = row_plan(s, s->block);
-  p.blk = split_plan(s, p.rp, s->block, 0);
+  p.blk = split_plan(s, p.rp, s->block, fa_rows(s, p.rp) ? 1 : 0);   // block items of the query-tiled kernel are long enough unsplit
   const int64_t blk_items = (int64_t)s->batch * s->h_kv * p.rp.qgroups * p.blk.splits;
   p.pre = split_plan(s, p.rp, max_prefix(s), s->num_splits, blk_items);
   p.rpre = partial_region(s, p.rp, p.pre, 0);

@@ -54,6 +54,19 @@ struct AttnArgs {
 constexpr int kStreamDepth = FB_STREAM_DEPTH;
 constexpr int kStreamTmax = FB_STREAM_TMAX;
 
+// Query-tiled kernel (fb_fa.hip) for large query groups: query tiles of 32 rows per wave
+// (a workgroup of kFaWaves waves covers 32 * kFaWaves * kFaQt rows); groups of at least
+// kFaMinRows rows.
+#ifndef FB_FA_QT
+#define FB_FA_QT 1
+#endif
+constexpr int kFaQt = FB_FA_QT;
+#ifndef FB_FA_WAVES
+#define FB_FA_WAVES 8
+#endif
+constexpr int kFaWaves = FB_FA_WAVES;
+constexpr int kFaMinRows = 256;
+
 enum CombineMode { kModeStep = 0, kModePrefixOnly = 1, kModeBlockOnly = 2, kModeLosa = 3 };
 
 struct CombineArgs {
@@ -76,6 +89,8 @@ struct CombineArgs {
 hipError_t launch_attn(const AttnArgs& a, bool bf16, hipStream_t st);
 bool stream_ok(const AttnArgs& a, const AttnSrc& s, int64_t max_tokens);
 hipError_t launch_stream(const AttnArgs& a, hipStream_t st);
+bool fa_ok(const AttnArgs& a, const AttnSrc& s);
+hipError_t launch_fa(const AttnArgs& a, hipStream_t st);
 hipError_t launch_combine(const CombineArgs& c, hipStream_t st);
 hipError_t launch_lse_merge(int64_t rows, int32_t d, const float* ao, const float* lo,
                             const float* ai, const float* li, void* af, int out_bf16,

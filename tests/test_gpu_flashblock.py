@@ -79,6 +79,10 @@ PREFIX_CASES = [
     ("mha_B64", 1, 2, 2, 128, 64, [2500], "bf16"),
     ("mha_B5_ragged", 3, 3, 1, 128, 5, [33, 0, 517], "bf16"),
     ("rows_tail_B40_g4", 1, 4, 1, 128, 40, [640], "bf16"),
+    # query groups of >= 256 rows (query-tiled kernel): ragged key tiles and query tiles
+    ("rows300_mha", 1, 2, 2, 128, 300, [1000], "bf16"),
+    ("rows400_gqa2", 1, 4, 2, 128, 200, [777], "bf16"),
+    ("rows260_varlen_empty", 2, 2, 1, 128, 130, [0, 2100], "bf16"),
     ("f32_d64", 2, 2, 2, 64, 4, [60, 77], "f32"),
     ("f32_d128_gqa", 1, 4, 2, 128, 7, [300], "f32"),
 ]
