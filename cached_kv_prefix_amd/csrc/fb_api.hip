@@ -373,7 +373,7 @@ fb_status check_losa(const losa_shape* ls) {
   const fb_shape& s = ls->s;
   if (ls->page_size < 1 || ls->topk < 1 || ls->n_active < 1 || ls->max_pages < 1) return FB_ERR_INVALID_ARG;
   if (ls->n_active > s.block) return FB_ERR_INVALID_ARG;
-  if (s.block > 1024 || ls->max_pages > 16384 || s.head_dim % 8 != 0) return FB_ERR_UNSUPPORTED;
+  if (s.block > 1024 || ls->max_pages > 16384 || s.head_dim % 8 != 0 || s.h_q > 1024) return FB_ERR_UNSUPPORTED;
   if (cdiv(max_prefix(&s), ls->page_size) > ls->max_pages) return FB_ERR_INVALID_ARG;
   return FB_OK;
 }
@@ -409,7 +409,7 @@ struct LosaPlan {
   RowPlan rp_sparse;
   SplitPlan sp_sparse;
   Region r_sparse, r_block;
-  size_t scores_off, active_off, ws_bytes;
+  size_t scores_off, active_off, loc_off, ws_bytes;
 };
 LosaPlan losa_plan(const losa_shape* ls) {
   LosaPlan p;
@@ -422,7 +422,8 @@ LosaPlan losa_plan(const losa_shape* ls) {
   p.scores_off = p.r_sparse.bytes + p.r_block.bytes;
   const size_t scores = (size_t)s->batch * s->h_q * ls->n_active * ls->max_pages * sizeof(double);
   p.active_off = align256(p.scores_off + scores);
-  p.ws_bytes = align256(p.active_off + (size_t)s->batch * ls->n_active * sizeof(int32_t));
+  p.loc_off = align256(p.active_off + (size_t)s->batch * ls->n_active * sizeof(int32_t));
+  p.ws_bytes = align256(p.loc_off + (size_t)s->batch * s->block * sizeof(double));
   return p;
 }
 
@@ -431,7 +432,8 @@ fb_status run_selection(const losa_shape* ls, const LosaPlan& p, const void* q_c
                         int32_t* union_pages, int32_t* union_count, void* ws, hipStream_t stream) {
   const LosaArgs la = losa_args(ls);
   double* scores = (double*)((char*)ws + p.scores_off);
-  if (hipError_t e = launch_locality(la, q_cur, q_prev, active, stream)) return hip_status(e);
+  double* loc = (double*)((char*)ws + p.loc_off);
+  if (hipError_t e = launch_locality(la, q_cur, q_prev, loc, active, stream)) return hip_status(e);
   if (hipError_t e = launch_quest_scores(la, q_cur, active, kmin, kmax, scores, stream)) return hip_status(e);
   if (hipError_t e = launch_topk(la, scores, topk_pages, stream)) return hip_status(e);
   return hip_status(launch_union(la, topk_pages, union_pages, union_count, stream));

@@ -111,7 +111,7 @@ struct LosaArgs {
 };
 hipError_t launch_page_meta(const LosaArgs& a, const void* k, void* kmin, void* kmax,
                             hipStream_t st);
-hipError_t launch_locality(const LosaArgs& a, const void* qc, const void* qp,
+hipError_t launch_locality(const LosaArgs& a, const void* qc, const void* qp, double* loc,
                            int32_t* active, hipStream_t st);
 hipError_t launch_quest_scores(const LosaArgs& a, const void* qc, const int32_t* active,
                                const void* kmin, const void* kmax, double* scores,

@@ -40,22 +40,23 @@ __device__ __forceinline__ uint64_t order_key(double s) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-// Exclusive scan of one value per thread (blockDim.x == 256) through LDS.
-__device__ __forceinline__ int block_excl_scan(int v, int* tmp) {
-  tmp[threadIdx.x] = v;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int t = 0; t < 256; ++t) {
-      const int x = tmp[t];
-      tmp[t] = run;
-      run += x;
-    }
-    tmp[256] = run;
+// Inclusive scan of one value per thread over a 256-thread block: a shuffle scan inside
+// each wave, then the wave totals through LDS (tmp holds 4 ints).  Every thread gets its
+// inclusive prefix; *total receives the block sum.
+__device__ __forceinline__ int block_incl_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
   }
+  if (lane == 63) tmp[w] = v;
   __syncthreads();
-  const int r = tmp[threadIdx.x];
-  return r;
+  int before = 0;
+  for (int i = 0; i < w; ++i) before += tmp[i];
+  *total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+  __syncthreads();
+  return v + before;
 }
 
 }  // namespace
@@ -80,10 +81,19 @@ __global__ void __launch_bounds__(256) page_meta_kernel(const LosaArgs a, const 
   }
   for (int t = t0; t < t1; ++t) {
     const int64_t base = ((int64_t)(seq0 + t) * a.h_kv + hk) * a.d + c * 8;
+    float x[8];
+    if (a.bf16) {
+      const u16x8 v = *(const u16x8*)((const uint16_t*)k + base);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = bf16_to_f32(v[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = ((const float*)k)[base + e];
+    }
+#pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float x = (float)load_elem(k, base + e, a.bf16);
-      mn[e] = fminf(mn[e], x);
-      mx[e] = fmaxf(mx[e], x);
+      mn[e] = fminf(mn[e], x[e]);
+      mx[e] = fmaxf(mx[e], x[e]);
     }
   }
   const int64_t out = ((((int64_t)b * a.h_kv + hk) * nc + c) * a.max_pages + p) * 8;
@@ -98,54 +108,70 @@ __global__ void __launch_bounds__(256) page_meta_kernel(const LosaArgs a, const 
   }
 }
 
-// One workgroup (1024 threads) per sequence.  Heads are processed in groups whose
-// per-(token, head) sums fit in LDS; each group's sums are added to the token totals in
-// head order.
-__global__ void __launch_bounds__(1024) locality_kernel(const LosaArgs a, const void* qc, const void* qp,
-                                                        int32_t* active) {
-  constexpr int kLdsDoubles = 6144;
-  __shared__ double inner[kLdsDoubles];
-  __shared__ double total[1024];
-  __shared__ int sel[1024];
-  const int b = blockIdx.x;
-  const int B = a.B, H = a.h_q, d = a.d;
-  for (int i = threadIdx.x; i < B; i += blockDim.x) total[i] = 0.0;
-  const int hg = max(1, min(H, kLdsDoubles / B));
-  for (int h0 = 0; h0 < H; h0 += hg) {
-    const int nh = min(hg, H - h0);
-    __syncthreads();
-    for (int w = threadIdx.x; w < B * nh; w += blockDim.x) {
-      const int i = w / nh, hh = w % nh;
-      const int64_t base = (((int64_t)b * B + i) * H + h0 + hh) * d;
-      double s = 0.0;
+// Locality score, part 1: one wave per (sequence, token).  Lane h forms its head's sum
+// over d, left to right, of the squared query change in fp64 (both queries are exact in
+// fp64 and so is their difference); the heads' sums are then added in head order and the
+// total is divided by H d, exactly as the definition is written.
+__global__ void __launch_bounds__(64) locality_kernel(const LosaArgs a, const void* qc, const void* qp,
+                                                      double* loc) {
+  __shared__ double inner[1024];
+  const int i = blockIdx.x, b = blockIdx.y;
+  const int H = a.h_q, d = a.d, lane = threadIdx.x;
+  for (int h = lane; h < H; h += 64) {
+    const int64_t base = (((int64_t)b * a.B + i) * H + h) * d;
+    double acc = 0.0;
+    if (a.bf16 && d <= 128) {
+      // the whole row of both queries in flight at once
+      u16x8 xc[16], xp[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c)
+        if (8 * c < d) {
+          xc[c] = *(const u16x8*)((const uint16_t*)qc + base + 8 * c);
+          xp[c] = *(const u16x8*)((const uint16_t*)qp + base + 8 * c);
+        }
+#pragma unroll
+      for (int c = 0; c < 16; ++c)
+        if (8 * c < d)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const double df = (double)bf16_to_f32(xc[c][e]) - (double)bf16_to_f32(xp[c][e]);
+            acc = acc + df * df;
+          }
+    } else {
       for (int j = 0; j < d; ++j) {
         const double df = load_elem(qc, base + j, a.bf16) - load_elem(qp, base + j, a.bf16);
-        s = s + df * df;
+        acc = acc + df * df;
       }
-      inner[i * nh + hh] = s;
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < B; i += blockDim.x) {
-      double t = total[i];
-      for (int hh = 0; hh < nh; ++hh) t = t + inner[i * nh + hh];
-      total[i] = t;
-    }
+    inner[h] = acc;
   }
   __syncthreads();
-  const double inv = 1.0 / (double)(H * d);
-  for (int i = threadIdx.x; i < B; i += blockDim.x) total[i] = total[i] * inv;
+  if (lane == 0) {
+    double t = 0.0;
+    for (int h = 0; h < H; ++h) t = t + inner[h];
+    loc[(int64_t)b * a.B + i] = t / (double)(H * d);
+  }
+}
+
+// Locality score, part 2: the active set of each sequence, the n_active largest scores
+// (ties to the lower token), listed ascending.
+__global__ void __launch_bounds__(256) active_kernel(const LosaArgs a, const double* loc, int32_t* active) {
+  __shared__ double sc[1024];
+  __shared__ int sel[1024];
+  const int b = blockIdx.x, B = a.B;
+  for (int i = threadIdx.x; i < B; i += 256) sc[i] = loc[(int64_t)b * B + i];
   __syncthreads();
-  for (int i = threadIdx.x; i < B; i += blockDim.x) {
-    const double si = total[i];
+  for (int i = threadIdx.x; i < B; i += 256) {
+    const double si = sc[i];
     int rank = 0;
     for (int j = 0; j < B; ++j) {
-      const double sj = total[j];
+      const double sj = sc[j];
       rank += (sj > si || (sj == si && j < i)) ? 1 : 0;
     }
     sel[i] = rank < a.n_active ? 1 : 0;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < B; i += blockDim.x) {
+  for (int i = threadIdx.x; i < B; i += 256) {
     if (!sel[i]) continue;
     int pos = 0;
     for (int j = 0; j < i; ++j) pos += sel[j];
@@ -153,137 +179,239 @@ __global__ void __launch_bounds__(1024) locality_kernel(const LosaArgs a, const 
   }
 }
 
-// grid (page blocks of 256, h_kv, batch); a thread scores one page for every active row of
-// the KV head's query heads, eight rows at a time, summing over d left to right.
+// QUEST page scores.  grid (page blocks of 256 * QPP, h_kv, batch); a thread scores QPP
+// pages for the active rows of the KV head's query heads, 8 rows at a time.  With
+// q+ = max(q, 0) and q- = min(q, 0) (held in LDS as fp64 pairs),
+//   q * (q >= 0 ? kmax : kmin) = fma(q-, kmin, q+ * kmax)
+// exactly (one product is zero, the other is exact in fp64), summed over d left to right.
+constexpr int kQpp = 2;
 __global__ void __launch_bounds__(256) quest_score_kernel(const LosaArgs a, const void* qc, const int32_t* active,
                                                           const void* kmin, const void* kmax, double* scores) {
-  __shared__ double qs[8][256];
+  __shared__ __attribute__((aligned(16))) double qpn[8][256][2];
   const int b = blockIdx.z, hk = blockIdx.y;
-  const int p = blockIdx.x * 256 + threadIdx.x;
+  const int p0 = (blockIdx.x * 256 + threadIdx.x) * kQpp;
   int seq0, n;
   seq_of(a, b, seq0, n);
   const int P = (n + a.page_size - 1) / a.page_size;
   const int d = a.d, nc = d / 8;
   const int R = a.G * a.n_active;
+  const int64_t mbase = (((int64_t)b * a.h_kv + hk) * nc) * a.max_pages * 8;
   for (int r0 = 0; r0 < R; r0 += 8) {
     const int nr = min(8, R - r0);
     __syncthreads();
-    for (int w = threadIdx.x; w < nr * d; w += 256) {
+    for (int w = threadIdx.x; w < 8 * d; w += 256) {
       const int rr = w / d, j = w % d;
-      const int r = r0 + rr;
-      const int h = hk * a.G + r / a.n_active;
-      const int tok = active[b * a.n_active + r % a.n_active];
-      qs[rr][j] = load_elem(qc, (((int64_t)b * a.B + tok) * a.h_q + h) * d + j, a.bf16);
+      double q = 0.0;
+      if (rr < nr) {
+        const int r = r0 + rr;
+        const int h = hk * a.G + r / a.n_active;
+        const int tok = active[b * a.n_active + r % a.n_active];
+        q = load_elem(qc, (((int64_t)b * a.B + tok) * a.h_q + h) * d + j, a.bf16);
+      }
+      qpn[rr][j][0] = q > 0.0 ? q : 0.0;
+      qpn[rr][j][1] = q < 0.0 ? q : 0.0;
     }
     __syncthreads();
-    if (p >= P) continue;
-    double acc[8];
+    if (p0 >= P) continue;
+    double acc[kQpp][8];
 #pragma unroll
-    for (int rr = 0; rr < 8; ++rr) acc[rr] = 0.0;
-    const int64_t mbase = (((int64_t)b * a.h_kv + hk) * nc) * a.max_pages * 8;
+    for (int u = 0; u < kQpp; ++u)
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) acc[u][rr] = 0.0;
     for (int c = 0; c < nc; ++c) {
-      const int64_t off = mbase + ((int64_t)c * a.max_pages + p) * 8;
-      double kn[8], kx[8];
-      if (a.bf16) {
-        const u16x8 vn = *(const u16x8*)((const uint16_t*)kmin + off);
-        const u16x8 vx = *(const u16x8*)((const uint16_t*)kmax + off);
+      double kn[kQpp][8], kx[kQpp][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          kn[e] = (double)bf16_to_f32(vn[e]);
-          kx[e] = (double)bf16_to_f32(vx[e]);
-        }
-      } else {
+      for (int u = 0; u < kQpp; ++u) {
+        const int64_t off = mbase + ((int64_t)c * a.max_pages + min(p0 + u, P - 1)) * 8;
+        if (a.bf16) {
+          const u16x8 vn = *(const u16x8*)((const uint16_t*)kmin + off);
+          const u16x8 vx = *(const u16x8*)((const uint16_t*)kmax + off);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          kn[e] = (double)((const float*)kmin)[off + e];
-          kx[e] = (double)((const float*)kmax)[off + e];
+          for (int e = 0; e < 8; ++e) {
+            kn[u][e] = (double)bf16_to_f32(vn[e]);
+            kx[u][e] = (double)bf16_to_f32(vx[e]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            kn[u][e] = (double)((const float*)kmin)[off + e];
+            kx[u][e] = (double)((const float*)kmax)[off + e];
+          }
         }
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
+      for (int rr = 0; rr < 8; ++rr)
 #pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-          const double qv = qs[rr][c * 8 + e];
-          acc[rr] = acc[rr] + qv * (qv >= 0.0 ? kx[e] : kn[e]);
+        for (int e = 0; e < 8; ++e) {
+          const double qp_ = qpn[rr][c * 8 + e][0], qn_ = qpn[rr][c * 8 + e][1];
+#pragma unroll
+          for (int u = 0; u < kQpp; ++u) acc[u][rr] = acc[u][rr] + __builtin_fma(qn_, kn[u][e], qp_ * kx[u][e]);
         }
     }
-    for (int rr = 0; rr < nr; ++rr) {
-      const int r = r0 + rr;
-      const int h = hk * a.G + r / a.n_active;
-      const int ai = r % a.n_active;
-      scores[(((int64_t)b * a.h_q + h) * a.n_active + ai) * a.max_pages + p] = acc[rr];
+#pragma unroll
+    for (int u = 0; u < kQpp; ++u) {
+      if (p0 + u >= P) continue;
+      for (int rr = 0; rr < nr; ++rr) {
+        const int r = r0 + rr;
+        const int h = hk * a.G + r / a.n_active;
+        const int ai = r % a.n_active;
+        scores[(((int64_t)b * a.h_q + h) * a.n_active + ai) * a.max_pages + p0 + u] = acc[u][rr];
+      }
     }
   }
 }
 
+__device__ __forceinline__ uint64_t wave_and64(uint64_t x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)x, o), hi = __shfl_xor((uint32_t)(x >> 32), o);
+    x &= ((uint64_t)hi << 32) | lo;
+  }
+  return x;
+}
+__device__ __forceinline__ uint64_t wave_or64(uint64_t x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)x, o), hi = __shfl_xor((uint32_t)(x >> 32), o);
+    x |= ((uint64_t)hi << 32) | lo;
+  }
+  return x;
+}
+
 // One workgroup per (b, h, active row): exact top-k by (score desc, page asc) with an
-// 8-pass MSB-first radix select on order-preserving 64-bit keys held in LDS; ties at the
-// threshold go to the lowest page indices; output ascending, padded with -1.
+// MSB-first radix select (8-bit digits) on order-preserving 64-bit keys.  Thread t holds
+// the keys of pages t + 256 j in registers (coalesced loads).  Leading bytes common to all
+// keys are skipped; each remaining pass builds a 256-bucket histogram of the keys that
+// match the prefix so far, and a block scan over the buckets (highest digit first) picks
+// the digit of the k-th largest key.  The selection is then two LDS bitmaps (keys above
+// it, keys equal to it; one ballot per wave and j gives one 64-page word): equal keys are
+// taken lowest pages first, and the result is compacted in ascending page order.  Fewer
+// than k pages: all of them, padded with -1.
+template <int KPT>
 __global__ void __launch_bounds__(256) topk_kernel(const LosaArgs a, const double* scores, int32_t* topk_pages) {
-  __shared__ uint64_t key[16384];
-  __shared__ int hist[257];
-  __shared__ int scan[257];
-  __shared__ uint64_t s_prefix;
-  __shared__ int s_need;
+  constexpr int NW = 4 * KPT;                   // 64-page words of the bitmaps
+  __shared__ int hist[256];
+  __shared__ int tmp[4];
+  __shared__ int s_digit, s_above;
+  __shared__ unsigned long long s_and, s_or;
+  __shared__ uint64_t gt_bits[NW], eq_bits[NW];
   const int rid = blockIdx.x;                   // (b * h_q + h) * n_active + ai
   const int b = rid / (a.h_q * a.n_active);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int seq0, n;
   seq_of(a, b, seq0, n);
   const int P = (n + a.page_size - 1) / a.page_size;
   const int K = a.topk;
   int32_t* out = topk_pages + (int64_t)rid * K;
   if (P <= K) {
-    for (int t = threadIdx.x; t < K; t += 256) out[t] = t < P ? t : -1;
+    for (int t = tid; t < K; t += 256) out[t] = t < P ? t : -1;
     return;
   }
   const double* sc = scores + (int64_t)rid * a.max_pages;
-  for (int p = threadIdx.x; p < P; p += 256) key[p] = order_key(sc[p]);
-  if (threadIdx.x == 0) {
-    s_prefix = 0;
-    s_need = K;
+  uint64_t key[KPT];
+  // unconditional loads (clamped index), so that all of them are in flight at once
+  double raw[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) raw[j] = sc[min(tid + 256 * j, P - 1)];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) key[j] = tid + 256 * j < P ? order_key(raw[j]) : 0ull;
+  if (tid == 0) {
+    s_and = ~0ull;
+    s_or = 0ull;
   }
-  uint64_t pmask = 0;
-  for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 56 - 8 * pass;
-    for (int t = threadIdx.x; t < 256; t += 256) hist[t] = 0;
-    __syncthreads();
-    const uint64_t prefix = s_prefix;
-    for (int p = threadIdx.x; p < P; p += 256)
-      if ((key[p] & pmask) == prefix) atomicAdd(&hist[(key[p] >> shift) & 255], 1);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int need = s_need, above = 0, dg = 255;
-      for (; dg > 0; --dg) {
-        if (above + hist[dg] >= need) break;
-        above += hist[dg];
+  __syncthreads();
+  {
+    uint64_t ka = ~0ull, ko = 0ull;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if (tid + 256 * j < P) {
+        ka &= key[j];
+        ko |= key[j];
       }
-      s_need = need - above;
-      s_prefix = prefix | ((uint64_t)dg << shift);
+    ka = wave_and64(ka);
+    ko = wave_or64(ko);
+    if (lane == 0) {
+      atomicAnd(&s_and, (unsigned long long)ka);
+      atomicOr(&s_or, (unsigned long long)ko);
     }
+  }
+  __syncthreads();
+  const uint64_t diff = s_and ^ s_or;
+  int pass0 = 0;
+  while (pass0 < 8 && ((diff >> (56 - 8 * pass0)) & 255) == 0) ++pass0;
+  uint64_t pmask = pass0 == 0 ? 0ull : (pass0 == 8 ? ~0ull : ~0ull << (64 - 8 * pass0));
+  uint64_t prefix = s_and & pmask;
+  int need = K;
+  for (int pass = pass0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    hist[tid] = 0;
+    __syncthreads();
+    // when every matching lane of a wave has the same digit (common in the leading
+    // passes) the wave adds its count with one atomic
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const bool match = tid + 256 * j < P && (key[j] & pmask) == prefix;
+      const int dg = (int)((key[j] >> shift) & 255);
+      const uint64_t m = __ballot(match);
+      if (m) {
+        const int leader = __ffsll((unsigned long long)m) - 1;
+        const int ldg = __builtin_amdgcn_readlane(dg, leader);
+        if (__ballot(match && dg == ldg) == m) {
+          if (lane == leader) atomicAdd(&hist[ldg], (int)__popcll(m));
+        } else if (match) {
+          atomicAdd(&hist[dg], 1);
+        }
+      }
+    }
+    __syncthreads();
+    // thread t looks at digit 255 - t: inclusive count of keys with a digit >= 255 - t
+    const int c = hist[255 - tid];
+    int total;
+    const int cum = block_incl_scan(c, tmp, &total);
+    if (cum >= need && cum - c < need) {
+      s_digit = 255 - tid;
+      s_above = cum - c;
+    }
+    __syncthreads();
+    need -= s_above;
+    prefix |= (uint64_t)s_digit << shift;
     pmask |= (uint64_t)255 << shift;
     __syncthreads();
   }
-  const uint64_t T = s_prefix;
-  const int need_eq = s_need;                    // keys equal to T to take, lowest pages first
-  const int per = (P + 255) / 256;
-  const int p0 = min(P, (int)threadIdx.x * per), p1 = min(P, p0 + per);
-  int eq = 0, gt = 0;
-  for (int p = p0; p < p1; ++p) {
-    eq += key[p] == T;
-    gt += key[p] > T;
-  }
-  const int eq_before = block_excl_scan(eq, scan);
-  const int take_eq = max(0, min(eq, need_eq - eq_before));
-  __syncthreads();
-  int pos = block_excl_scan(gt + take_eq, scan);
-  int te = take_eq;
-  for (int p = p0; p < p1; ++p) {
-    if (key[p] > T) {
-      out[pos++] = p;
-    } else if (key[p] == T && te > 0) {
-      out[pos++] = p;
-      --te;
+  const uint64_t T = prefix;                    // the k-th largest key; `need` equal keys go in
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const bool valid = tid + 256 * j < P;
+    const uint64_t g = __ballot(valid && key[j] > T), e = __ballot(valid && key[j] == T);
+    if (lane == 0) {
+      gt_bits[4 * j + w] = g;
+      eq_bits[4 * j + w] = e;
     }
+  }
+  __syncthreads();
+  // word t (pages 64 t ..): equal keys before it, then this word's share of them
+  const int wi = tid < NW ? tid : 0;
+  const uint64_t eqw = tid < NW ? eq_bits[wi] : 0ull;
+  int total;
+  const int eq_before = block_incl_scan(__popcll(eqw), tmp, &total) - __popcll(eqw);
+  uint64_t take = 0ull;
+  {
+    int left = need - eq_before;
+    uint64_t m = eqw;
+    while (left > 0 && m) {
+      const uint64_t low = m & (~m + 1);
+      take |= low;
+      m ^= low;
+      --left;
+    }
+  }
+  const uint64_t selw = (tid < NW ? gt_bits[wi] : 0ull) | take;
+  int pos = block_incl_scan(__popcll(selw), tmp, &total) - __popcll(selw);
+  uint64_t m = selw;
+  while (m) {
+    const int bit = __ffsll((unsigned long long)m) - 1;
+    m &= m - 1;
+    out[pos++] = 64 * tid + bit;
   }
 }
 
@@ -308,8 +436,8 @@ __global__ void __launch_bounds__(256) union_kernel(const LosaArgs a, const int3
   const int w0 = min(nw, (int)threadIdx.x * per), w1 = min(nw, w0 + per);
   int cnt = 0;
   for (int w = w0; w < w1; ++w) cnt += __popc(bits[w]);
-  int pos = block_excl_scan(cnt, scan);
-  const int total = scan[256];
+  int total;
+  int pos = block_incl_scan(cnt, scan, &total) - cnt;
   int32_t* out = union_pages + ((int64_t)b * a.h_kv + hk) * a.max_union;
   for (int w = w0; w < w1; ++w) {
     uint32_t m = bits[w];
@@ -329,21 +457,27 @@ hipError_t launch_page_meta(const LosaArgs& a, const void* k, void* kmin, void* 
   return hipGetLastError();
 }
 
-hipError_t launch_locality(const LosaArgs& a, const void* qc, const void* qp, int32_t* active, hipStream_t st) {
-  hipLaunchKernelGGL(locality_kernel, dim3(a.batch), dim3(1024), 0, st, a, qc, qp, active);
+hipError_t launch_locality(const LosaArgs& a, const void* qc, const void* qp, double* loc, int32_t* active,
+                           hipStream_t st) {
+  hipLaunchKernelGGL(locality_kernel, dim3(a.B, a.batch), dim3(64), 0, st, a, qc, qp, loc);
+  if (hipError_t e = hipGetLastError()) return e;
+  hipLaunchKernelGGL(active_kernel, dim3(a.batch), dim3(256), 0, st, a, loc, active);
   return hipGetLastError();
 }
 
 hipError_t launch_quest_scores(const LosaArgs& a, const void* qc, const int32_t* active, const void* kmin,
                                const void* kmax, double* scores, hipStream_t st) {
-  dim3 grid((unsigned)((a.max_pages + 255) / 256), a.h_kv, a.batch);
+  dim3 grid((unsigned)((a.max_pages + 256 * kQpp - 1) / (256 * kQpp)), a.h_kv, a.batch);
   hipLaunchKernelGGL(quest_score_kernel, grid, dim3(256), 0, st, a, qc, active, kmin, kmax, scores);
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const LosaArgs& a, const double* scores, int32_t* topk_pages, hipStream_t st) {
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)(a.batch * a.h_q * a.n_active)), dim3(256), 0, st, a, scores,
-                     topk_pages);
+  const dim3 grid((unsigned)(a.batch * a.h_q * a.n_active));
+  if (a.max_pages <= 256 * 32)
+    hipLaunchKernelGGL(topk_kernel<32>, grid, dim3(256), 0, st, a, scores, topk_pages);
+  else
+    hipLaunchKernelGGL(topk_kernel<64>, grid, dim3(256), 0, st, a, scores, topk_pages);
   return hipGetLastError();
 }
 
