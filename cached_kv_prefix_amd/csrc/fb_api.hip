@@ -81,7 +81,7 @@ struct SplitPlan {
 // last to be dispatched, and waiting for a free CU they would add their whole latency to
 // the end of the launch.
 bool stream_rows(const fb_shape* s, const RowPlan& rp) {
-  return s->dtype == FB_BF16 && s->head_dim == 128 && rp.rows <= 32;
+  return s->dtype == FB_BF16 && s->head_dim == 128 && rp.rows <= 32 * kStreamRtMax;
 }
 // Large query groups run on the query-tiled kernel: 128 * kFaQt rows per work item.
 bool fa_rows(const fb_shape* s, const RowPlan& rp) {
@@ -105,8 +105,10 @@ SplitPlan split_plan(const fb_shape* s, const RowPlan& rp, int64_t max_keys, int
     if (stream_rows(s, rp)) {
       want = std::max<int64_t>(1, (FB_STREAM_TARGET_ITEMS - reserved) / items);
     } else if (fa_rows(s, rp)) {
-      const int64_t fa_items = (int64_t)s->batch * s->h_kv * cdiv(rp.rows, 32 * kFaWaves * kFaQt);
-      want = std::max<int64_t>(1, (FB_FA_TARGET_ITEMS + fa_items / 2) / fa_items);
+      // resident workgroups: 2 per CU with 4 waves, 1 with 8; aim for two rounds of them
+      const int64_t fa_items = (int64_t)s->batch * s->h_kv * cdiv(rp.rows, fa_rows_per_item(rp.rows));
+      const int64_t target = (fa_waves(rp.rows) == 4 ? 2 : 1) * FB_FA_TARGET_ITEMS;
+      want = std::max<int64_t>(1, (target + fa_items / 2) / fa_items);
     } else {
       want = cdiv(kTargetItems, items);
     }

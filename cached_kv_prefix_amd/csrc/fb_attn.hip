@@ -373,7 +373,7 @@ hipError_t launch_attn(const AttnArgs& a, bool bf16, hipStream_t st) {
     const int rows = a.src0.n_splits ? a.src0.rows : a.src1.rows;
     if (rows >= kFaMinRows && fa_ok(a, a.src0) && fa_ok(a, a.src1)) return launch_fa(a, st);
     const bool s0 = stream_ok(a, a.src0, a.max_seqlen), s1 = stream_ok(a, a.src1, a.max_seqlen);
-    const bool mixed = a.src0.pages != nullptr && a.src1.n_splits > 0;
+    const bool mixed = a.src0.n_splits > 0 && a.src0.pages != nullptr && a.src1.n_splits > 0;
     if (s0 && s1 && !mixed) return launch_stream(a, st);
     if (s0 && a.src0.n_splits > 0) {
       AttnArgs a0 = a;
@@ -382,6 +382,7 @@ hipError_t launch_attn(const AttnArgs& a, bool bf16, hipStream_t st) {
       AttnArgs a1 = a;
       a1.src0.n_splits = 0;
       a1.src0.qgroups = 0;
+      if (a1.src1.rows >= kFaMinRows && fa_ok(a1, a1.src1)) return launch_fa(a1, st);
       return launch_generic(a1, bf16, st);
     }
   }

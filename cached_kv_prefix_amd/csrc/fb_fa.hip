@@ -1,6 +1,6 @@
-// Query-tiled attention for large query groups (the video-sized block and its prefix pass):
-// the pass is a dense contraction (4680 query rows per head), so it is bound by the
-// matrix cores rather than by HBM.  Same split-KV partial-result format as the other
+// Query-tiled attention for query groups of more than 32 rows: the video-sized block and
+// its prefix pass (4680 rows per head, a dense contraction bound by the matrix cores) and
+// grouped-query prefixes (4 query heads x 32 block tokens share each K / V tile).  Same split-KV partial-result format as the other
 // attention kernels; fb_combine.hip reduces the chunks and merges.
 //
 // What is computed ("Resumo Técnico: FlashBlock", §2 Mecanismo Central): for the query
@@ -8,10 +8,11 @@
 //   m = max_j s_j,  l = sum_j 2^(s_j - m),  O = sum_j 2^(s_j - m) v_j,  s_j = log2(e) scale <q, k_j>.
 //
 // gfx950 design:
-//   * a workgroup = W waves owns 32 * W * QT query rows; a wave owns 32 * QT rows (QT
+//   * a workgroup = W waves owns 32 * W * QT query rows (W = 4 for groups of up to 128
+//     rows, such as 4 query heads x 32 block tokens, else 8); a wave owns 32 * QT rows (QT
 //     query tiles), so every K / V operand read from LDS feeds QT matrix instructions;
-//   * keys advance in 64-key tiles, double-buffered in LDS and shared by the W waves (8:
-//     256 query rows per K / V tile): the next tiles are loaded into registers (16-byte
+//   * keys advance in 64-key tiles, double-buffered in LDS and shared by the W waves: the
+//     next tiles are loaded into registers (16-byte
 //     row pieces, buffer loads) while the current one is computed, then written to the
 //     other LDS buffer; one barrier per tile;
 //   * software pipeline: S of tile t + 1 is issued before the softmax of tile t, so the
@@ -46,7 +47,7 @@ __device__ __forceinline__ int fa_qtiles(const AttnSrc& S, int rows_per_wg) {
   return (S.rows + rows_per_wg - 1) / rows_per_wg;
 }
 
-template <int QT, int W>
+template <int QT, int W, bool DEEP>
 __global__ void __launch_bounds__(64 * W, QT == 1 && W == 4 ? 2 : 1) attn_fa_kernel(const AttnArgs A) {
   constexpr int D = 128;
   constexpr int ROWS_WG = 32 * W * QT;
@@ -123,18 +124,18 @@ __global__ void __launch_bounds__(64 * W, QT == 1 && W == 4 ? 2 : 1) attn_fa_ker
     k_dst[u] = r * 256 + ((p_chunk ^ (r & 15)) << 4);
     v_dst[u] = r * 256 + ((p_chunk ^ (4 * (r & 3))) << 4);
   }
-  u32x4 kreg[NP], vreg[NP];
+  u32x4 kreg[2][NP], vreg[2][NP];   // two staging sets (the second one only when DEEP)
   const int ntile = (kend - kbeg + kFaTile - 1) / kFaTile;
 
   // Buffer loads: rows past the chunk end read as zero (and fetch nothing).
-#define FA_LOAD_K(T)                                                                             \
-  _Pragma("unroll") for (int u = 0; u < NP; ++u) kreg[u] = __builtin_bit_cast(u32x4,             \
+#define FA_LOAD_K(T, SET)                                                                        \
+  _Pragma("unroll") for (int u = 0; u < NP; ++u) kreg[SET][u] = __builtin_bit_cast(u32x4,        \
       __builtin_amdgcn_raw_buffer_load_b128(krs, (T) * kFaTile * (int)tstride * 2 + g_off + u * g_step, 0, 0));
-#define FA_LOAD_V(T)                                                                             \
-  _Pragma("unroll") for (int u = 0; u < NP; ++u) vreg[u] = __builtin_bit_cast(u32x4,             \
+#define FA_LOAD_V(T, SET)                                                                        \
+  _Pragma("unroll") for (int u = 0; u < NP; ++u) vreg[SET][u] = __builtin_bit_cast(u32x4,        \
       __builtin_amdgcn_raw_buffer_load_b128(vrs, (T) * kFaTile * (int)tstride * 2 + g_off + u * g_step, 0, 0));
-#define FA_STORE_K(BUF) _Pragma("unroll") for (int u = 0; u < NP; ++u) *(u32x4*)(lds[BUF] + k_dst[u]) = kreg[u];
-#define FA_STORE_V(BUF) _Pragma("unroll") for (int u = 0; u < NP; ++u) *(u32x4*)(lds[BUF] + kFaTileBytes + v_dst[u]) = vreg[u];
+#define FA_STORE_K(BUF, SET) _Pragma("unroll") for (int u = 0; u < NP; ++u) *(u32x4*)(lds[BUF] + k_dst[u]) = kreg[SET][u];
+#define FA_STORE_V(BUF, SET) _Pragma("unroll") for (int u = 0; u < NP; ++u) *(u32x4*)(lds[BUF] + kFaTileBytes + v_dst[u]) = vreg[SET][u];
 
   // K operand read: key 32 s + ql, chunk 2 i2 + g -> stored chunk (2 i2) ^ (g ^ (ql & 15)).
   const int k_src = ql * 256;
@@ -216,26 +217,67 @@ __global__ void __launch_bounds__(64 * W, QT == 1 && W == 4 ? 2 : 1) attn_fa_ker
   // Every tile but the last is full, so the loop body has no masking; the last tile is
   // finished after the loop.  The loop is unrolled by two so that the two score sets
   // swap roles without register copies.
-  f32x16 acc[QT][2], acc_n[QT][2];
   bf16x8 pb[QT][4];
-  FA_LOAD_K(0);
-  FA_LOAD_V(0);
-  FA_STORE_K(0);
-  FA_STORE_V(0);
-  FA_LOAD_K(1);
-  FA_STORE_K(1);
+  if constexpr (DEEP) {
+    // Memory-bound groups (a few query tiles per K / V tile): no score pipelining, but two
+    // tiles of loads in flight.  Iteration t loads tile t + 2 into staging set t&1,
+    // computes tile t from LDS buffer t&1, then stores tile t + 1 (loaded an iteration
+    // earlier) into buffer (t+1)&1, last read in iteration t - 1; one barrier per tile.
+    f32x16 acc[QT][2];
+#define FA_DEEP_ITER(T, CUR)                                                                     \
+  {                                                                                              \
+    FA_LOAD_K((T) + 2, CUR);                                                                     \
+    FA_LOAD_V((T) + 2, CUR);                                                                     \
+    FA_QK(acc, lds[CUR]);                                                                        \
+    if ((T) == ntile - 1) {                                                                      \
+      const int kvalid = kend - kbeg - (T) * kFaTile;                                            \
+      if (kvalid < kFaTile)                                                                      \
+        _Pragma("unroll") for (int s = 0; s < 2; ++s)                                            \
+          _Pragma("unroll") for (int r = 0; r < 16; ++r) {                                       \
+            const int key = 32 * s + 8 * (r >> 2) + 4 * g + (r & 3);                             \
+            if (key >= kvalid) _Pragma("unroll") for (int qi = 0; qi < QT; ++qi) acc[qi][s][r] = kNegInf; \
+          }                                                                                      \
+    }                                                                                            \
+    FA_SOFTMAX(acc, pb);                                                                         \
+    FA_PV(pb, lds[CUR] + kFaTileBytes);                                                          \
+    FA_STORE_K((CUR) ^ 1, (CUR) ^ 1);                                                            \
+    FA_STORE_V((CUR) ^ 1, (CUR) ^ 1);                                                            \
+    __syncthreads();                                                                             \
+  }
+    FA_LOAD_K(0, 0);
+    FA_LOAD_V(0, 0);
+    FA_LOAD_K(1, 1);
+    FA_LOAD_V(1, 1);
+    FA_STORE_K(0, 0);
+    FA_STORE_V(0, 0);
+    __syncthreads();
+    int t = 0;
+    for (; t + 1 < ntile; t += 2) {
+      FA_DEEP_ITER(t, 0);
+      FA_DEEP_ITER(t + 1, 1);
+    }
+    if (t < ntile) FA_DEEP_ITER(t, 0);
+#undef FA_DEEP_ITER
+  } else {
+  f32x16 acc[QT][2], acc_n[QT][2];
+  FA_LOAD_K(0, 0);
+  FA_LOAD_V(0, 0);
+  FA_STORE_K(0, 0);
+  FA_STORE_V(0, 0);
+  FA_LOAD_K(1, 0);
+  FA_STORE_K(1, 0);
   __syncthreads();
   FA_QK(acc, lds[0]);
   __syncthreads();   // K buffer 0 is rewritten in iteration 0
 #define FA_ITER(T, CUR, ACC_C, ACC_N)                                                            \
   {                                                                                              \
-    FA_LOAD_K((T) + 2);                                                                          \
-    FA_LOAD_V((T) + 1);                                                                          \
+    FA_LOAD_K((T) + 2, 0);                                                                       \
+    FA_LOAD_V((T) + 1, 0);                                                                       \
     FA_QK(ACC_N, lds[(CUR) ^ 1]);                                                                \
     FA_SOFTMAX(ACC_C, pb);                                                                       \
     FA_PV(pb, lds[CUR] + kFaTileBytes);                                                          \
-    FA_STORE_K(CUR);                                                                             \
-    FA_STORE_V((CUR) ^ 1);                                                                       \
+    FA_STORE_K(CUR, 0);                                                                          \
+    FA_STORE_V((CUR) ^ 1, 0);                                                                    \
     __syncthreads();                                                                             \
   }
   int t = 0;
@@ -268,6 +310,7 @@ __global__ void __launch_bounds__(64 * W, QT == 1 && W == 4 ? 2 : 1) attn_fa_ker
     }
     FA_SOFTMAX(acc, pb);
     FA_PV(pb, lds[(ntile - 1) & 1] + kFaTileBytes);
+  }
   }
 #undef FA_LOAD_K
 #undef FA_LOAD_V
@@ -312,14 +355,19 @@ bool fa_ok(const AttnArgs& a, const AttnSrc& s) {
 }
 
 hipError_t launch_fa(const AttnArgs& a, hipStream_t st) {
-  const int64_t rows_wg = 32 * kFaWaves * kFaQt;
+  const int rows = a.src0.n_splits ? a.src0.rows : a.src1.rows;
+  const int64_t rows_wg = fa_rows_per_item(rows);
   auto items = [&](const AttnSrc& s) -> int64_t {
     return s.n_splits ? (int64_t)s.n_splits * a.batch * a.h_kv * ((s.rows + rows_wg - 1) / rows_wg) : 0;
   };
   const int64_t n = items(a.src0) + items(a.src1);
   if (n == 0) return hipSuccess;
   if (n >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_fa_kernel<kFaQt, kFaWaves>), dim3((unsigned)n), dim3(64 * kFaWaves), 0, st, a);
+  // up to 128 rows the pass streams K / V (deep prefetch); larger groups are matrix bound
+  if (fa_waves(rows) == 4)
+    hipLaunchKernelGGL((attn_fa_kernel<kFaQt, 4, true>), dim3((unsigned)n), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_fa_kernel<kFaQt, 8, false>), dim3((unsigned)n), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 

@@ -53,19 +53,17 @@ struct AttnArgs {
 #endif
 constexpr int kStreamDepth = FB_STREAM_DEPTH;
 constexpr int kStreamTmax = FB_STREAM_TMAX;
+constexpr int kStreamRtMax = 2;                 // 32-row query tiles per wave (rows <= 64)
 
-// Query-tiled kernel (fb_fa.hip) for large query groups: query tiles of 32 rows per wave
-// (a workgroup of kFaWaves waves covers 32 * kFaWaves * kFaQt rows); groups of at least
-// kFaMinRows rows.
+// Query-tiled kernel (fb_fa.hip) for query groups of more than 64 rows: a wave owns
+// 32 * kFaQt rows and a workgroup fa_waves(rows) waves (4 up to 128 rows, else 8).
 #ifndef FB_FA_QT
 #define FB_FA_QT 1
 #endif
 constexpr int kFaQt = FB_FA_QT;
-#ifndef FB_FA_WAVES
-#define FB_FA_WAVES 8
-#endif
-constexpr int kFaWaves = FB_FA_WAVES;
-constexpr int kFaMinRows = 256;
+constexpr int kFaMinRows = 65;
+inline int fa_waves(int rows) { return rows <= 128 * kFaQt ? 4 : 8; }
+inline int fa_rows_per_item(int rows) { return 32 * kFaQt * fa_waves(rows); }
 
 enum CombineMode { kModeStep = 0, kModePrefixOnly = 1, kModeBlockOnly = 2, kModeLosa = 3 };
 
