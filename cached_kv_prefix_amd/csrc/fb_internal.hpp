@@ -35,6 +35,25 @@ struct AttnSrc {
   float* pml;                 // partial m,l [batch][h_kv][n_splits][rows][2]
 };
 
+enum CombineMode { kModeStep = 0, kModePrefixOnly = 1, kModeBlockOnly = 2, kModeLosa = 3 };
+
+struct CombineArgs {
+  int32_t mode;
+  int32_t batch, B, h_q, h_kv, G, d;
+  // prefix partials (src0) and how many splits of each group are valid
+  const float* po; const float* pml; int32_t p_rows; int32_t p_splits; int32_t p_chunk;
+  const int32_t* cu; int32_t n_uniform;
+  const int32_t* page_count; int32_t page_size;
+  // block partials (src1)
+  const float* bo; const float* bml; int32_t b_rows; int32_t b_splits; int32_t b_chunk;
+  const uint8_t* mask;                 // step: [batch][h_q], null = recompute all
+  const int32_t* m_upd; int32_t tau;   // step: threshold rule evaluated in place of mask
+  const int32_t* active; int32_t n_active;   // LoSA
+  float* cache_a; float* cache_l;      // step/LoSA cache, or prefix-only outputs
+  float* ain; float* lin;              // block-only outputs
+  void* a_full; int32_t out_bf16; float* l_full;
+};
+
 struct AttnArgs {
   const void* q;              // [batch][B][h_q][d]
   int32_t batch, B, h_q, h_kv, G, d;
@@ -65,24 +84,6 @@ constexpr int kFaMinRows = 65;
 inline int fa_waves(int rows) { return rows <= 128 * kFaQt ? 4 : 8; }
 inline int fa_rows_per_item(int rows) { return 32 * kFaQt * fa_waves(rows); }
 
-enum CombineMode { kModeStep = 0, kModePrefixOnly = 1, kModeBlockOnly = 2, kModeLosa = 3 };
-
-struct CombineArgs {
-  int32_t mode;
-  int32_t batch, B, h_q, h_kv, G, d;
-  // prefix partials (src0) and how many splits of each group are valid
-  const float* po; const float* pml; int32_t p_rows; int32_t p_splits; int32_t p_chunk;
-  const int32_t* cu; int32_t n_uniform;
-  const int32_t* page_count; int32_t page_size;
-  // block partials (src1)
-  const float* bo; const float* bml; int32_t b_rows; int32_t b_splits; int32_t b_chunk;
-  const uint8_t* mask;                 // step: [batch][h_q], null = recompute all
-  const int32_t* m_upd; int32_t tau;   // step: threshold rule evaluated in place of mask
-  const int32_t* active; int32_t n_active;   // LoSA
-  float* cache_a; float* cache_l;      // step/LoSA cache, or prefix-only outputs
-  float* ain; float* lin;              // block-only outputs
-  void* a_full; int32_t out_bf16; float* l_full;
-};
 
 hipError_t launch_attn(const AttnArgs& a, bool bf16, hipStream_t st);
 bool stream_ok(const AttnArgs& a, const AttnSrc& s, int64_t max_tokens);
