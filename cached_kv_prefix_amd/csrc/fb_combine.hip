@@ -5,15 +5,14 @@
 namespace fb {
 
 // One wave per output row (b, i, h); lanes own dims lane + 64 e.
-template <int E>
+template <int E, int UP, int UB>
 __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs C) {
-  constexpr int U = 8;
   const int lane = threadIdx.x & 63;
   const int rowid = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   if (rowid >= C.batch * C.B * C.h_q) return;
-  RowState<E, U> st;
-  row_issue<E, U>(C, rowid, lane, st);
-  row_finish<E, U>(C, lane, st);
+  RowState<E, UP, UB> st;
+  row_issue<E, UP, UB>(C, rowid, lane, st);
+  row_finish<E, UP, UB>(C, lane, st);
 }
 
 template <int E>
@@ -94,12 +93,30 @@ hipError_t launch_combine(const CombineArgs& c, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   if (rows > INT32_MAX - 4) return hipErrorInvalidValue;   // row indices are 32-bit
   const dim3 grid((unsigned)((rows + 3) / 4));
-  if (c.d <= 64)
-    hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(256), 0, st, c);
-  else if (c.d <= 128)
-    hipLaunchKernelGGL(combine_kernel<2>, grid, dim3(256), 0, st, c);
-  else
-    hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(256), 0, st, c);
+  // chunk loads issued up front: as many as the plan has (d = 128), else 8
+  const int up = c.p_splits <= 1 ? 1 : c.p_splits <= 2 ? 2 : c.p_splits <= 4 ? 4 : 8;
+  const bool ub1 = c.b_splits <= 1;
+  if (c.d <= 64) {
+    hipLaunchKernelGGL((combine_kernel<1, 8, 8>), grid, dim3(256), 0, st, c);
+  } else if (c.d <= 128) {
+#define FB_COMBINE_UB(UP)                                                                    \
+  if (ub1)                                                                                   \
+    hipLaunchKernelGGL((combine_kernel<2, UP, 1>), grid, dim3(256), 0, st, c);               \
+  else                                                                                       \
+    hipLaunchKernelGGL((combine_kernel<2, UP, 8>), grid, dim3(256), 0, st, c);
+    if (up == 1) {
+      FB_COMBINE_UB(1)
+    } else if (up == 2) {
+      FB_COMBINE_UB(2)
+    } else if (up == 4) {
+      FB_COMBINE_UB(4)
+    } else {
+      FB_COMBINE_UB(8)
+    }
+#undef FB_COMBINE_UB
+  } else {
+    hipLaunchKernelGGL((combine_kernel<4, 8, 8>), grid, dim3(256), 0, st, c);
+  }
   return hipGetLastError();
 }
 

@@ -138,17 +138,20 @@ __device__ __forceinline__ int n_chunks(int n_keys, int chunk) { return (n_keys 
 // partial load of the row (prefix, block, cached row) is issued before the reuse
 // decision is known.  Issuing several rows before finishing any keeps their round trips
 // in flight together.
-template <int E, int U>
+template <int E, int UP, int UB>
 struct RowState {
-  RowPartials<E, U> PP, PB;
+  RowPartials<E, UP> PP;
+  RowPartials<E, UB> PB;
   float cached[E], cached_l;
   int64_t roff, pslot0, bslot0;
   int rowid, b, i, h, hk, jg, prow, nk;
   bool fresh;
 };
 
-template <int E, int U>
-__device__ __forceinline__ void row_issue(const CombineArgs& C, int rowid, int lane, RowState<E, U>& st) {
+// UP / UB: prefix / block chunks whose loads are issued up front (further chunks, if
+// any, are read during the reduction).
+template <int E, int UP, int UB>
+__device__ __forceinline__ void row_issue(const CombineArgs& C, int rowid, int lane, RowState<E, UP, UB>& st) {
   const int h = rowid % C.h_q;
   const int i = (rowid / C.h_q) % C.B;
   const int b = rowid / (C.h_q * C.B);
@@ -179,9 +182,9 @@ __device__ __forceinline__ void row_issue(const CombineArgs& C, int rowid, int l
   st.bslot0 = (int64_t)(b * C.h_kv + hk) * C.b_splits;
   st.cached_l = kNegInf;
   if (has_prefix && C.p_splits > 0)
-    issue_partials<E, U>(C.po, C.pml, st.pslot0, C.p_rows, st.prow, C.p_splits, d, lane, st.PP);
+    issue_partials<E, UP>(C.po, C.pml, st.pslot0, C.p_rows, st.prow, C.p_splits, d, lane, st.PP);
   if (C.mode != kModePrefixOnly && C.b_splits > 0)
-    issue_partials<E, U>(C.bo, C.bml, st.bslot0, C.b_rows, jg * C.B + i, C.b_splits, d, lane, st.PB);
+    issue_partials<E, UB>(C.bo, C.bml, st.bslot0, C.b_rows, jg * C.B + i, C.b_splits, d, lane, st.PB);
   if (has_prefix && C.mode != kModePrefixOnly) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -205,8 +208,8 @@ __device__ __forceinline__ void row_issue(const CombineArgs& C, int rowid, int l
     st.nk = C.cu[b + 1] - C.cu[b];
 }
 
-template <int E, int U>
-__device__ __forceinline__ void row_finish(const CombineArgs& C, int lane, const RowState<E, U>& st) {
+template <int E, int UP, int UB>
+__device__ __forceinline__ void row_finish(const CombineArgs& C, int lane, const RowState<E, UP, UB>& st) {
   const int d = C.d;
   const bool has_prefix = C.mode != kModeBlockOnly;
   float ao[E], ai[E], af[E];
@@ -216,7 +219,7 @@ __device__ __forceinline__ void row_finish(const CombineArgs& C, int lane, const
   if (has_prefix) {
     if (st.fresh) {
       const int n = C.p_splits > 0 ? min(n_chunks(st.nk, C.p_chunk), C.p_splits) : 0;
-      reduce_chunks<E, U>(st.PP, C.po, C.pml, st.pslot0, C.p_rows, st.prow, n, d, lane, ao, lo);
+      reduce_chunks<E, UP>(st.PP, C.po, C.pml, st.pslot0, C.p_rows, st.prow, n, d, lane, ao, lo);
       float* ca = C.cache_a + st.roff;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
@@ -235,7 +238,7 @@ __device__ __forceinline__ void row_finish(const CombineArgs& C, int lane, const
   // block-internal part
   {
     const int n = C.b_splits > 0 ? min(n_chunks(C.B, C.b_chunk), C.b_splits) : 0;
-    reduce_chunks<E, U>(st.PB, C.bo, C.bml, st.bslot0, C.b_rows, st.jg * C.B + st.i, n, d, lane, ai, li);
+    reduce_chunks<E, UB>(st.PB, C.bo, C.bml, st.bslot0, C.b_rows, st.jg * C.B + st.i, n, d, lane, ai, li);
   }
   if (C.mode == kModeBlockOnly) {
     float* pa = C.ain + st.roff;

@@ -27,6 +27,10 @@
 //     they are the long ones, so the short block items fill in behind them.
 #include "fb_attn_common.hpp"
 
+#ifndef FB_FA_BIG
+#define FB_FA_BIG 0
+#endif
+
 namespace fb {
 
 namespace {
@@ -366,6 +370,10 @@ hipError_t launch_fa(const AttnArgs& a, hipStream_t st) {
   // up to 128 rows the pass streams K / V (deep prefetch); larger groups are matrix bound
   if (fa_waves(rows) == 4)
     hipLaunchKernelGGL((attn_fa_kernel<kFaQt, 4, true>), dim3((unsigned)n), dim3(256), 0, st, a);
+  else if (FB_FA_BIG == 1)
+    hipLaunchKernelGGL((attn_fa_kernel<2, 4, true>), dim3((unsigned)n), dim3(256), 0, st, a);
+  else if (FB_FA_BIG == 2)
+    hipLaunchKernelGGL((attn_fa_kernel<2, 4, false>), dim3((unsigned)n), dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((attn_fa_kernel<kFaQt, 8, false>), dim3((unsigned)n), dim3(512), 0, st, a);
   return hipGetLastError();
