@@ -90,14 +90,6 @@ __global__ void __launch_bounds__(256, FB_STREAM_WG_PER_CU) attn_stream_kernel(c
   if (kbeg >= si.n_keys) return;
   const int kend = min(si.n_keys, kbeg + S.chunk);
   const int rows = S.rows;                          // <= 32 * RT
-  if (S.m_upd) {
-    if (S.m_upd[b] < S.tau) return;
-  } else if (S.mask) {
-    bool any = false;
-    for (int j = 0; j < A.G; ++j)
-      if (j * S.rows_per_head < rows) any |= S.mask[b * A.h_q + hk * A.G + j] == 0;
-    if (!any) return;
-  }
 
   // This wave's keys: sub-tiles w, w + 4, ... of the chunk (chunk = 128 * TMAX at most);
   // sub-tile j of the wave starts at key kw0 + 128 j.
@@ -225,6 +217,17 @@ __global__ void __launch_bounds__(256, FB_STREAM_WG_PER_CU) attn_stream_kernel(c
   if (nsub > 0) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) FB_ISSUE(s, s);
+  }
+  // The reuse decision is read once the first loads are in flight: an item whose heads all
+  // reuse the cache leaves (its loads only fill registers), every other item has saved a
+  // round trip.
+  if (S.m_upd) {
+    if (S.m_upd[b] < S.tau) return;
+  } else if (S.mask) {
+    bool any = false;
+    for (int j = 0; j < A.G; ++j)
+      if (j * S.rows_per_head < rows) any |= S.mask[b * A.h_q + hk * A.G + j] == 0;
+    if (!any) return;
   }
 
 #define FB_STEP(J)                                                                            \
