@@ -182,8 +182,9 @@ __global__ void __launch_bounds__(256) active_kernel(const LosaArgs a, const dou
 // QUEST page scores.  grid (page blocks of 256 * QPP, h_kv, batch); a thread scores QPP
 // pages for the active rows of the KV head's query heads, 8 rows at a time.  With
 // q+ = max(q, 0) and q- = min(q, 0) (held in LDS as fp64 pairs),
-//   q * (q >= 0 ? kmax : kmin) = fma(q-, kmin, q+ * kmax)
-// exactly (one product is zero, the other is exact in fp64), summed over d left to right.
+//   acc + q * (q >= 0 ? kmax : kmin) == fma(q-, kmin, fma(q+, kmax, acc))
+// exactly: one of the two products is zero, the other is exact in fp64 and rounds once, as
+// in the left-to-right fp64 sum over d of the definition.
 constexpr int kQpp = 2;
 __global__ void __launch_bounds__(256) quest_score_kernel(const LosaArgs a, const void* qc, const int32_t* active,
                                                           const void* kmin, const void* kmax, double* scores) {
@@ -245,7 +246,7 @@ __global__ void __launch_bounds__(256) quest_score_kernel(const LosaArgs a, cons
         for (int e = 0; e < 8; ++e) {
           const double qp_ = qpn[rr][c * 8 + e][0], qn_ = qpn[rr][c * 8 + e][1];
 #pragma unroll
-          for (int u = 0; u < kQpp; ++u) acc[u][rr] = acc[u][rr] + __builtin_fma(qn_, kn[u][e], qp_ * kx[u][e]);
+          for (int u = 0; u < kQpp; ++u) acc[u][rr] = __builtin_fma(qn_, kn[u][e], __builtin_fma(qp_, kx[u][e], acc[u][rr]));
         }
     }
 #pragma unroll
