@@ -143,7 +143,7 @@ def flushed_step_times(fn, n=10):
     sink = torch.empty((), dtype=torch.float32, device="cuda")
     out = []
     for _ in range(n):
-        torch.sum(scratch, dtype=torch.float32, out=sink)
+        torch.sum(scratch, dim=0, out=sink)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         fn(None)
