@@ -81,7 +81,7 @@ struct SplitPlan {
 // last to be dispatched, and waiting for a free CU they would add their whole latency to
 // the end of the launch.
 bool stream_rows(const fb_shape* s, const RowPlan& rp) {
-  return s->dtype == FB_BF16 && s->head_dim == 128 && rp.rows <= 32 * kStreamRtMax;
+  return s->dtype == FB_BF16 && s->head_dim == 128 && rp.rows <= 32;
 }
 // Large query groups run on the query-tiled kernel: 128 * kFaQt rows per work item.
 bool fa_rows(const fb_shape* s, const RowPlan& rp) {

@@ -72,15 +72,14 @@ struct AttnArgs {
 #endif
 constexpr int kStreamDepth = FB_STREAM_DEPTH;
 constexpr int kStreamTmax = FB_STREAM_TMAX;
-constexpr int kStreamRtMax = 2;                 // 32-row query tiles per wave (rows <= 64)
 
-// Query-tiled kernel (fb_fa.hip) for query groups of more than 64 rows: a wave owns
+// Query-tiled kernel (fb_fa.hip) for query groups of more than 32 rows: a wave owns
 // 32 * kFaQt rows and a workgroup fa_waves(rows) waves (4 up to 128 rows, else 8).
 #ifndef FB_FA_QT
 #define FB_FA_QT 1
 #endif
 constexpr int kFaQt = FB_FA_QT;
-constexpr int kFaMinRows = 65;
+constexpr int kFaMinRows = 33;
 inline int fa_waves(int rows) { return rows <= 128 * kFaQt ? 4 : 8; }
 inline int fa_rows_per_item(int rows) { return 32 * kFaQt * fa_waves(rows); }
 

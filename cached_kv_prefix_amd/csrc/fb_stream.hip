@@ -1,4 +1,4 @@
-// Streaming split-KV attention for query groups of at most 64 rows (the FlashBlock
+// Streaming split-KV attention for query groups of at most 32 rows (the FlashBlock
 // prefix pass of a dLLM block, the block pass at small B, and the LoSA sparse pass over
 // the union pages).  Same partial-result format as fb_attn.hip.
 //
@@ -34,12 +34,7 @@
 //     stored with their 16-byte chunks XOR-swizzled by (key & 3) so the four rows of one
 //     transposed read fall in distinct LDS banks;
 //   * a paged source (LoSA union, page size >= 16) reads the wave-uniform page indices of
-//     a sub-tile with scalar loads, which do not queue behind the vector loads;
-//   * groups of 33-64 rows: every wave holds both 32-row query tiles for its keys (RT = 2),
-//     the queries then live in LDS (one copy for the four waves), and every K / V operand
-//     read feeds two matrix instructions.
-#include <algorithm>
-
+//     a sub-tile with scalar loads, which do not queue behind the vector loads.
 #include "fb_attn_common.hpp"
 
 #ifndef FB_STREAM_SRC1_FIRST
@@ -63,19 +58,15 @@ __device__ __forceinline__ s16x4 lds_read_tr(const unsigned char* p) {
 
 }  // namespace
 
-template <int NS, int TMAX, bool PAGED, int RT>
+template <int NS, int TMAX, bool PAGED>
 __global__ void __launch_bounds__(256, FB_STREAM_WG_PER_CU) attn_stream_kernel(const AttnArgs A) {
   constexpr int D = 128;
   constexpr int VB = 32 * D * 2;                    // K (or V) bytes of one 32-key sub-tile
   static_assert(NS >= 1 && NS <= 3, "pipeline depth (16 ops per sub-tile, counter max 63)");
-  static_assert(RT == 1 || RT == 2, "32-row query tiles per wave (at four, the 128 x 128 accumulators no longer fit)");
   constexpr int RING = 4 * 2 * VB;                  // one K and one V slot per wave
-  constexpr int RED = 4 * 32 * D * 4;               // final combine (one row tile at a time)
+  constexpr int RED = 4 * 32 * D * 4;               // final combine
   __shared__ __attribute__((aligned(16))) unsigned char vring[RING > RED ? RING : RED];
   __shared__ float red_m[4 * 32], red_l[4 * 32];
-  // RT > 1: the group's query rows in LDS (row r at r*256, 16-byte chunk c stored at
-  // c ^ (r & 15)), read as the B operand; one copy serves the four waves.
-  __shared__ __attribute__((aligned(16))) unsigned char qlds[RT > 1 ? RT * 32 * 256 : 16];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform (SGPR)
@@ -89,7 +80,7 @@ __global__ void __launch_bounds__(256, FB_STREAM_WG_PER_CU) attn_stream_kernel(c
   const int kbeg = split * S.chunk;
   if (kbeg >= si.n_keys) return;
   const int kend = min(si.n_keys, kbeg + S.chunk);
-  const int rows = S.rows;                          // <= 32 * RT
+  const int rows = S.rows;                          // <= 32
 
   // This wave's keys: sub-tiles w, w + 4, ... of the chunk (chunk = 128 * TMAX at most);
   // sub-tile j of the wave starts at key kw0 + 128 j.
@@ -98,35 +89,18 @@ __global__ void __launch_bounds__(256, FB_STREAM_WG_PER_CU) attn_stream_kernel(c
   const int nsub = __builtin_amdgcn_readfirstlane(kend > kw0 ? (kend - kw0 + 127) / 128 : 0);
 
   // Query fragment (B operand of S^T = K Q^T): lane holds d = 16*i + 8*g + 0..7.
-  bf16x8 qf[RT == 1 ? D / 16 : 1];
-  if constexpr (RT == 1) {
-    if (ql < rows) {
-      const int j = ql / S.rows_per_head, i = ql % S.rows_per_head;
-      const int tok = S.row_tok ? S.row_tok[b * S.rows_per_head + i] : i;
-      const int h = hk * A.G + j;
-      const uint16_t* qp = (const uint16_t*)A.q + ((int64_t)(b * A.B + tok) * A.h_q + h) * D + 8 * g;
+  bf16x8 qf[D / 16];
+  if (ql < rows) {
+    const int j = ql / S.rows_per_head, i = ql % S.rows_per_head;
+    const int tok = S.row_tok ? S.row_tok[b * S.rows_per_head + i] : i;
+    const int h = hk * A.G + j;
+    const uint16_t* qp = (const uint16_t*)A.q + ((int64_t)(b * A.B + tok) * A.h_q + h) * D + 8 * g;
 #pragma unroll
-      for (int i2 = 0; i2 < D / 16; ++i2) qf[i2] = *(const bf16x8*)(qp + 16 * i2);
-    } else {
-#pragma unroll
-      for (int i2 = 0; i2 < D / 16; ++i2) qf[i2] = bf16x8{};
-    }
+    for (int i2 = 0; i2 < D / 16; ++i2) qf[i2] = *(const bf16x8*)(qp + 16 * i2);
   } else {
 #pragma unroll
-    for (int k = 0; k < 2 * RT; ++k) {
-      const int idx = tid + 256 * k, row = idx >> 4, c = idx & 15;
-      u32x4 x = u32x4{};
-      if (row < rows) {
-        const int j = row / S.rows_per_head, i = row % S.rows_per_head;
-        const int tok = S.row_tok ? S.row_tok[b * S.rows_per_head + i] : i;
-        x = *(const u32x4*)((const uint16_t*)A.q + ((int64_t)(b * A.B + tok) * A.h_q + hk * A.G + j) * D + 8 * c);
-      }
-      *(u32x4*)(qlds + row * 256 + ((c ^ (row & 15)) << 4)) = x;
-    }
-    __syncthreads();
+    for (int i2 = 0; i2 < D / 16; ++i2) qf[i2] = bf16x8{};
   }
-  const int q_src = ql * 256;                       // + 32*256 per row tile
-  const int q_x = g ^ (ql & 15);
 
   const int64_t tstride = (int64_t)A.h_kv * D;
   const uint16_t* kbase = (const uint16_t*)S.k + (int64_t)si.seq0 * tstride + hk * D;
@@ -204,15 +178,10 @@ __global__ void __launch_bounds__(256, FB_STREAM_WG_PER_CU) attn_stream_kernel(c
     }                                                                                         \
   } while (0)
 
-  float m_run[RT], l_run[RT];
-  f32x16 o[RT][D / 32];
+  float m_run = kNegInf, l_run = 0.f;
+  f32x16 o[D / 32];
 #pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    m_run[r] = kNegInf;
-    l_run[r] = 0.f;
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) o[r][t] = f32x16{};
-  }
+  for (int t = 0; t < D / 32; ++t) o[t] = f32x16{};
 
   if (nsub > 0) {
 #pragma unroll
@@ -241,67 +210,56 @@ _Pragma("unroll") for (int u = 0; u < 8; ++u) {                                 
     const uint32_t vm = vmask[s];                                                           \
     FB_ISSUE((J) + NS, s);                                                                  \
                                                                                             \
-    f32x16 acc[RT];                                                                         \
-_Pragma("unroll") for (int r = 0; r < RT; ++r) acc[r] = f32x16{};                           \
+    f32x16 acc = f32x16{};                                                                  \
 _Pragma("unroll")                                                                           \
     for (int i2 = 0; i2 < D / 16; ++i2) {                                                   \
       const bf16x8 ka = *(const bf16x8*)(kslot + k_src_row + (((2 * i2) ^ k_src_x) << 4));  \
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[i2], acc, 0, 0, 0);             \
+    }                                                                                       \
+    float mx = kNegInf;                                                                     \
+    if (vm == 0xffffffffu) {                                                                \
 _Pragma("unroll")                                                                           \
-      for (int r = 0; r < RT; ++r) {                                                        \
-        const bf16x8 qb = RT == 1 ? qf[i2 % (RT == 1 ? D / 16 : 1)]                         \
-            : *(const bf16x8*)(qlds + r * 32 * 256 + q_src + (((2 * i2) ^ q_x) << 4));      \
-        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb, acc[r], 0, 0, 0);          \
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[r]);                                  \
+    } else {                                                                                \
+_Pragma("unroll")                                                                           \
+      for (int r = 0; r < 16; ++r) {                                                        \
+        if (!((vm >> (8 * (r >> 2) + 4 * g + (r & 3))) & 1u)) acc[r] = kNegInf;             \
+        mx = fmaxf(mx, acc[r]);                                                             \
       }                                                                                     \
     }                                                                                       \
-    bf16x8 pb[RT][2];                                                                       \
+    mx = wave_max_xor32(mx) * A.scale_log2;                                                 \
+    /* lazy reference: raise m_run only when a score exceeds it by more than 2^8 */          \
+    const bool need_ = mx > m_run + 8.0f;                                                   \
+    if (__any(need_)) {                                                                     \
+      const float m_new = need_ ? mx : m_run;                                               \
+      const float alpha = exp2_or_zero(m_run - m_new);                                      \
+      l_run *= alpha;                                                                       \
 _Pragma("unroll")                                                                           \
-    for (int r = 0; r < RT; ++r) {                                                          \
-      float mx = kNegInf;                                                                   \
-      if (vm == 0xffffffffu) {                                                              \
-_Pragma("unroll")                                                                           \
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, acc[r][e]);                             \
-      } else {                                                                              \
-_Pragma("unroll")                                                                           \
-        for (int e = 0; e < 16; ++e) {                                                      \
-          if (!((vm >> (8 * (e >> 2) + 4 * g + (e & 3))) & 1u)) acc[r][e] = kNegInf;        \
-          mx = fmaxf(mx, acc[r][e]);                                                        \
-        }                                                                                   \
-      }                                                                                     \
-      mx = wave_max_xor32(mx) * A.scale_log2;                                               \
-      /* lazy reference: raise m_run only when a score exceeds it by more than 2^8 */        \
-      const bool need_ = mx > m_run[r] + 8.0f;                                              \
-      if (__any(need_)) {                                                                   \
-        const float m_new = need_ ? mx : m_run[r];                                          \
-        const float alpha = exp2_or_zero(m_run[r] - m_new);                                 \
-        l_run[r] *= alpha;                                                                  \
-_Pragma("unroll")                                                                           \
-        for (int t = 0; t < D / 32; ++t) o[r][t] *= alpha;                                  \
-        m_run[r] = m_new;                                                                   \
-      }                                                                                     \
-      const float m_use = m_run[r] == kNegInf ? 0.f : m_run[r];                             \
-      float ps = 0.f;                                                                       \
-_Pragma("unroll")                                                                           \
-      for (int c = 0; c < 2; ++c)                                                           \
-_Pragma("unroll")                                                                           \
-        for (int jj = 0; jj < 8; ++jj) {                                                    \
-          const float p_ = fast_exp2(fmaf(acc[r][8 * c + jj], A.scale_log2, -m_use));        \
-          ps += p_;                                                                         \
-          pb[r][c][jj] = (__bf16)p_;                                                        \
-        }                                                                                   \
-      ps += __shfl_xor(ps, 32);                                                             \
-      l_run[r] += ps;                                                                       \
+      for (int t = 0; t < D / 32; ++t) o[t] *= alpha;                                       \
+      m_run = m_new;                                                                        \
     }                                                                                       \
+    const float m_use = m_run == kNegInf ? 0.f : m_run;                                     \
+    float sv[16];                                                                           \
+    float ps = 0.f;                                                                         \
+_Pragma("unroll")                                                                           \
+    for (int r = 0; r < 16; ++r) {                                                          \
+      sv[r] = fast_exp2(fmaf(acc[r], A.scale_log2, -m_use));                                \
+      ps += sv[r];                                                                          \
+    }                                                                                       \
+    ps += __shfl_xor(ps, 32);                                                               \
+    l_run += ps;                                                                            \
 _Pragma("unroll")                                                                           \
     for (int c = 0; c < 2; ++c) {                                                           \
+      bf16x8 pb;                                                                            \
+_Pragma("unroll")                                                                           \
+      for (int jj = 0; jj < 8; ++jj) pb[jj] = (__bf16)sv[8 * c + jj];                       \
       const unsigned char* a = tr_base + c * 16 * 256;                                      \
 _Pragma("unroll")                                                                           \
       for (int t = 0; t < D / 32; ++t) {                                                    \
         const s16x4 lo = lds_read_tr(a + tr_off[t]);                                        \
         const s16x4 hi = lds_read_tr(a + 8 * 256 + tr_off[t]);                              \
         const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)); \
-_Pragma("unroll")                                                                           \
-        for (int r = 0; r < RT; ++r)                                                        \
-          o[r][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[r][c], o[r][t], 0, 0, 0); \
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[t], 0, 0, 0);              \
       }                                                                                     \
     }                                                                                       \
     __builtin_amdgcn_sched_barrier(0);                                                     \
@@ -323,94 +281,81 @@ _Pragma("unroll")                                                               
 #undef FB_STEP
 #undef FB_ISSUE
 
-  // Combine the four waves (disjoint key ranges, same query rows), one 32-row tile at a
-  // time, then write the partial rows.
+  // Combine the four waves (disjoint key ranges, same query rows), then write the partial.
+  __syncthreads();
+  float* red = (float*)vring;
+  if (g == 0) {
+    red_m[w * 32 + ql] = m_run;
+    red_l[w * 32 + ql] = l_run;
+  }
+  __syncthreads();
+  {
+    float M = kNegInf;
+    for (int s = 0; s < 4; ++s) M = fmaxf(M, red_m[s * 32 + ql]);
+    const float Mu = M == kNegInf ? 0.f : M;
+    const float f = exp2_or_zero(m_run - Mu);
+    float* dst = red + (w * 32 + ql) * D;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 x;
+        x[0] = o[t][4 * r4 + 0] * f;
+        x[1] = o[t][4 * r4 + 1] * f;
+        x[2] = o[t][4 * r4 + 2] * f;
+        x[3] = o[t][4 * r4 + 3] * f;
+        *(f32x4*)(dst + 32 * t + 8 * r4 + 4 * g) = x;
+      }
+  }
+  __syncthreads();
   const int64_t slot = (int64_t)(b * A.h_kv + hk) * S.n_splits + split;
   float* po = S.po + slot * rows * D;
   float* pml = S.pml + slot * rows * 2;
-  float* red = (float*)vring;
-#pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    __syncthreads();
-    if (g == 0) {
-      red_m[w * 32 + ql] = m_run[r];
-      red_l[w * 32 + ql] = l_run[r];
-    }
-    __syncthreads();
-    {
-      float M = kNegInf;
-      for (int s = 0; s < 4; ++s) M = fmaxf(M, red_m[s * 32 + ql]);
-      const float Mu = M == kNegInf ? 0.f : M;
-      const float f = exp2_or_zero(m_run[r] - Mu);
-      float* dst = red + (w * 32 + ql) * D;
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          f32x4 x;
-          x[0] = o[r][t][4 * r4 + 0] * f;
-          x[1] = o[r][t][4 * r4 + 1] * f;
-          x[2] = o[r][t][4 * r4 + 2] * f;
-          x[3] = o[r][t][4 * r4 + 3] * f;
-          *(f32x4*)(dst + 32 * t + 8 * r4 + 4 * g) = x;
-        }
-    }
-    __syncthreads();
-    const int rt_rows = min(32, rows - 32 * r);
-    for (int idx = tid; idx < rt_rows * (D / 4); idx += 256) {
-      const int rr = idx / (D / 4), c4 = idx % (D / 4);
-      f32x4 sum = f32x4{};
-      for (int s = 0; s < 4; ++s) sum += *(const f32x4*)(red + (s * 32 + rr) * D + 4 * c4);
-      *(f32x4*)(po + (int64_t)(32 * r + rr) * D + 4 * c4) = sum;
-    }
-    for (int rr = tid; rr < rt_rows; rr += 256) {
-      float M = kNegInf;
-      for (int s = 0; s < 4; ++s) M = fmaxf(M, red_m[s * 32 + rr]);
-      const float Mu = M == kNegInf ? 0.f : M;
-      float l = 0.f;
-      for (int s = 0; s < 4; ++s) l += exp2_or_zero(red_m[s * 32 + rr] - Mu) * red_l[s * 32 + rr];
-      pml[(32 * r + rr) * 2 + 0] = M;
-      pml[(32 * r + rr) * 2 + 1] = l;
-    }
+  for (int idx = tid; idx < rows * (D / 4); idx += 256) {
+    const int r = idx / (D / 4), c4 = idx % (D / 4);
+    f32x4 sum = f32x4{};
+    for (int s = 0; s < 4; ++s) sum += *(const f32x4*)(red + (s * 32 + r) * D + 4 * c4);
+    *(f32x4*)(po + (int64_t)r * D + 4 * c4) = sum;
+  }
+  for (int r = tid; r < rows; r += 256) {
+    float M = kNegInf;
+    for (int s = 0; s < 4; ++s) M = fmaxf(M, red_m[s * 32 + r]);
+    const float Mu = M == kNegInf ? 0.f : M;
+    float l = 0.f;
+    for (int s = 0; s < 4; ++s) l += exp2_or_zero(red_m[s * 32 + r] - Mu) * red_l[s * 32 + r];
+    pml[r * 2 + 0] = M;
+    pml[r * 2 + 1] = l;
   }
 }
 
-// The streaming kernel covers bf16, d = 128, at most 64 rows per group (two 32-row
-// tiles per wave), chunks of at most 128 * kStreamTmax keys; a paged source needs pages
-// of at least 16 tokens.
+// The streaming kernel covers bf16, d = 128, at most 32 rows per group, chunks of at most
+// 128 * kStreamTmax keys; a paged source needs pages of at least 16 tokens.
 bool stream_ok(const AttnArgs& a, const AttnSrc& s, int64_t max_tokens) {
   if (s.n_splits == 0) return true;
-  if (a.d != 128 || s.rows > 32 * kStreamRtMax || s.chunk > 128 * kStreamTmax) return false;
+  if (a.d != 128 || s.rows > 32 || s.chunk > 128 * kStreamTmax) return false;
   // K offsets are 32-bit: a wave's keys (contiguous) or a whole sequence (paged)
   const int64_t span = s.pages ? max_tokens : s.chunk;
   if (span * a.h_kv * 128 * 2 >= ((int64_t)1 << 31)) return false;
   return !s.pages || s.page_size >= 16;
 }
 
-template <int RT>
-static hipError_t launch_stream_rt(const AttnArgs& a, hipStream_t st) {
-  dim3 grid(a.h_kv, a.src0.n_splits + a.src1.n_splits, a.batch);
+hipError_t launch_stream(const AttnArgs& a, hipStream_t st) {
+  const int gy = a.src0.n_splits + a.src1.n_splits;
+  if (gy == 0) return hipSuccess;
+  dim3 grid(a.h_kv, gy, a.batch);
   const bool paged = a.src0.n_splits && a.src0.pages != nullptr;   // only the LoSA sparse source is paged
+  if (paged && a.src1.n_splits) return hipErrorInvalidValue;
   if (paged) {
-    hipLaunchKernelGGL((attn_stream_kernel<kStreamDepth, kStreamTmax, true, RT>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_stream_kernel<kStreamDepth, kStreamTmax, true>), grid, dim3(256), 0, st, a);
   } else if (FB_STREAM_SRC1_FIRST && a.src1.n_splits) {
     AttnArgs sw = a;
     sw.src0 = a.src1;
     sw.src1 = a.src0;
-    hipLaunchKernelGGL((attn_stream_kernel<kStreamDepth, kStreamTmax, false, RT>), grid, dim3(256), 0, st, sw);
+    hipLaunchKernelGGL((attn_stream_kernel<kStreamDepth, kStreamTmax, false>), grid, dim3(256), 0, st, sw);
   } else {
-    hipLaunchKernelGGL((attn_stream_kernel<kStreamDepth, kStreamTmax, false, RT>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_stream_kernel<kStreamDepth, kStreamTmax, false>), grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();
-}
-
-hipError_t launch_stream(const AttnArgs& a, hipStream_t st) {
-  const int gy = a.src0.n_splits + a.src1.n_splits;
-  if (gy == 0) return hipSuccess;
-  if (a.src0.n_splits && a.src0.pages != nullptr && a.src1.n_splits) return hipErrorInvalidValue;
-  const int rows = std::max(a.src0.n_splits ? a.src0.rows : 0, a.src1.n_splits ? a.src1.rows : 0);
-  if (rows <= 32) return launch_stream_rt<1>(a, st);
-  return launch_stream_rt<2>(a, st);
 }
 
 }  // namespace fb
