@@ -270,6 +270,7 @@ def main():
         extra["block8_fresh_steps"] = fresh
         extra["cold_fresh_step_us"] = flushed_step_times(lambda tr: run_step(fb, shape, dev, bufs, m_fresh)) * 1e6
         extra["workloads"] = other_workloads(fb, args)
+        extra["context_sweep"] = context_sweep(fb, args)
     result = {
         "metric": "attn step µs & KV GB/s (B=32, 32k prefix, bf16); % of HBM/MFMA peak",
         "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -286,6 +287,48 @@ def main():
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(p)
     print(json.dumps(result))
+
+
+def context_sweep(fb, args, lengths=(102400, 204800, 409600, 819200)):
+    """Prefix lengths 100k -> 800k on the dLLM step shape (32 heads, d 128, B 32, bf16):
+    the always-fresh step and the mean step of an 8-step block under the threshold rule
+    (tau 4, M drawn as in the dLLM workload).  The growth of each with the context, as a
+    ratio, is the shape the FlashBlock pages claim (reuse roughly halves it).  Inputs are
+    drawn on the device from a seeded generator (N(0,1)/sqrt(128), rounded to bf16); the
+    kernels and split plans are the ones the parity tests cover."""
+    import torch
+    import synth
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    H, d, B = 32, 128, 32
+    m_all = torch.from_numpy(synth.dllm().extra["m_updated"]).cuda()   # [8 steps, 1]
+    out = []
+    steps = max(5, args.steps // 5)
+    for n in lengths:
+        def draw(*shape):
+            return (torch.randn(*shape, generator=gen, device="cuda") / np.sqrt(128.0)).to(torch.bfloat16)
+        dev = dict(q=draw(1, B, H, d), k=draw(n, H, d), v=draw(n, H, d), k_blk=draw(1, B, H, d),
+                   v_blk=draw(1, B, H, d))
+        shape = fb.make_shape(1, H, H, d, B, seqlen_k=n)
+        bufs = dict(ws=torch.empty(fb.workspace_size(shape), dtype=torch.uint8, device="cuda"),
+                    ca=torch.zeros((1, B, H, d), device="cuda"), cl=torch.zeros((1, B, H), device="cuda"),
+                    af=torch.zeros((1, B, H, d), dtype=torch.bfloat16, device="cuda"),
+                    lf=torch.zeros((1, B, H), device="cuda"), mask=torch.zeros((1, H), dtype=torch.uint8, device="cuda"))
+        fresh, _, _ = time_steps(lambda tr: run_step(fb, shape, dev, bufs, m_all[0], trace=tr), steps, 3)
+
+        def block(tr):
+            for s_ in range(8):
+                run_step(fb, shape, dev, bufs, m_all[s_], trace=tr)
+        blk, _, _ = time_steps(block, max(3, steps // 4), 1)
+        out.append({"prefix": n, "fresh_step_us": fresh * 1e6, "block8_mean_step_us": blk / 8 * 1e6,
+                    "fresh_kv_GBps": n * H * d * 4 / fresh / 1e9})
+        del dev, bufs
+        torch.cuda.empty_cache()
+    f0, f1 = out[0]["fresh_step_us"], out[-1]["fresh_step_us"]
+    b0, b1 = out[0]["block8_mean_step_us"], out[-1]["block8_mean_step_us"]
+    return {"points": out, "fresh_growth_us": f1 - f0, "block8_growth_us": b1 - b0,
+            "growth_ratio_block8_over_fresh": (b1 - b0) / (f1 - f0),
+            "fresh_steps_per_block": int(1 + (synth.dllm().extra["m_updated"][1:, 0] >= 4).sum())}
 
 
 def other_workloads(fb, args):
