@@ -104,3 +104,28 @@ def test_active_set_tie_to_higher_index_is_caught(monkeypatch):
         return np.array([np.sort(sorted(range(s.shape[1]), key=lambda i: (-s[b, i], -i))[:n]) for b in range(s.shape[0])])
     monkeypatch.setattr(OL, "active_set", bad)
     assert _fails(TL.test_active_set_ties_and_order)
+
+
+def test_residual_complement_off_by_one_is_caught(monkeypatch):
+    """A complement that drops the last unselected page breaks the refresh = full pin."""
+    import oracle.residual as OR
+    import tests.test_oracle_residual as TR
+    real = OR.complement_pages
+    monkeypatch.setattr(OR, "complement_pages", lambda sel, n: real(sel, n)[:-1])
+    assert _fails(TR.test_refresh_step_equals_full_attention)
+
+
+def test_residual_merge_dropping_a_part_is_caught(monkeypatch):
+    import oracle.residual as OR
+    import tests.test_oracle_residual as TR
+    monkeypatch.setattr(OR, "lse_merge3", lambda a1, l1, a2, l2, a3, l3: OA.lse_merge(a1, l1, a3, l3))
+    assert _fails(TR.test_refresh_step_equals_full_attention)
+
+
+def test_residual_reuse_that_recomputes_is_caught(monkeypatch):
+    """A step that refreshes the residual whatever the mask breaks the persistence pin."""
+    import oracle.residual as OR
+    import tests.test_oracle_residual as TR
+    real = OR.step
+    monkeypatch.setattr(TR, "step", lambda *a: real(*a[:8], np.zeros_like(a[8]), *a[9:]))
+    assert _fails(TR.test_stale_residual_persists_and_only_reusing_heads_keep_it)
