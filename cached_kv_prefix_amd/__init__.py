@@ -17,7 +17,8 @@ FB_BF16, FB_F32 = 0, 1
 STATUS = {0: "FB_OK", 1: "FB_ERR_INVALID_ARG", 2: "FB_ERR_UNSUPPORTED", 3: "FB_ERR_WORKSPACE", 5: "FB_ERR_HIP"}
 EXPORTS = ("fb_status_string", "fb_workspace_size", "fb_prefix_attn", "fb_block_attn", "fb_lse_merge",
            "fb_step", "fb_step_threshold", "fb_mask_threshold", "fb_mask_similarity", "fb_head_cosine", "losa_meta_bytes",
-           "losa_workspace_size", "losa_union_capacity", "losa_page_meta", "losa_select_union", "losa_step")
+           "losa_workspace_size", "losa_union_capacity", "losa_page_meta", "losa_select_union", "losa_step",
+           "fb_residual_workspace_size", "fb_residual_step")
 
 
 class FlashBlockError(RuntimeError):
@@ -36,6 +37,10 @@ class FbShape(C.Structure):
 class LosaShape(C.Structure):
     _fields_ = [("s", FbShape), ("page_size", C.c_int32), ("topk", C.c_int32), ("n_active", C.c_int32),
                 ("max_pages", C.c_int32)]
+
+
+class ResidualShape(C.Structure):
+    _fields_ = [("s", FbShape), ("page_size", C.c_int32), ("max_pages", C.c_int32), ("max_sel", C.c_int32)]
 
 
 class FbTrace(C.Structure):
@@ -57,6 +62,7 @@ def load(path: str | None = None):
     lib = C.CDLL(p)
     vp, i32, i64, f32, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
     sp, lp, tp = C.POINTER(FbShape), C.POINTER(LosaShape), C.POINTER(FbTrace)
+    rp = C.POINTER(ResidualShape)
     sig = {
         "fb_status_string": (C.c_char_p, [i32]),
         "fb_workspace_size": (sz, [sp]),
@@ -74,6 +80,8 @@ def load(path: str | None = None):
         "losa_page_meta": (i32, [lp, vp, vp, vp, vp]),
         "losa_select_union": (i32, [lp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "losa_step": (i32, [lp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, tp, vp]),
+        "fb_residual_workspace_size": (sz, [rp]),
+        "fb_residual_step": (i32, [rp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, tp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -120,6 +128,13 @@ def make_losa_shape(shape: FbShape, page_size=16, topk=64, n_active=8, max_pages
         n = shape.max_seqlen_k if shape.cu_seqlens_k else shape.seqlen_k
         max_pages = max(1, -(-n // page_size))
     return LosaShape(shape, page_size, topk, n_active, max_pages)
+
+
+def make_residual_shape(shape: FbShape, page_size=16, max_sel=None, max_pages=None) -> ResidualShape:
+    if max_pages is None:
+        n = shape.max_seqlen_k if shape.cu_seqlens_k else shape.seqlen_k
+        max_pages = max(1, -(-n // page_size))
+    return ResidualShape(shape, page_size, max_pages, max_pages if max_sel is None else max_sel)
 
 
 def make_trace(**events) -> FbTrace:
@@ -218,3 +233,17 @@ def losa_step(ls, q_cur, q_prev, k, v, k_blk, v_blk, kmin, kmax, cache_a, cache_
                             _ptr(active), _ptr(topk_pages), _ptr(union_pages), _ptr(union_count), _ptr(ws),
                             ws.numel() * ws.element_size(), None if trace is None else C.byref(trace),
                             _stream(stream)), "losa_step")
+
+
+def residual_workspace_size(rs: ResidualShape) -> int:
+    return int(load().fb_residual_workspace_size(C.byref(rs)))
+
+
+def residual_step(rs, q, k, v, k_blk, v_blk, sel_pages, sel_count, reuse_mask, cache_a, cache_l, a_full, l_full,
+                  ws, trace=None, stream=None):
+    _check(load().fb_residual_step(C.byref(rs), _ptr(q), _ptr(k), _ptr(v), _ptr(k_blk), _ptr(v_blk),
+                                   _ptr(sel_pages), _ptr(sel_count), _ptr(reuse_mask), _ptr(cache_a),
+                                   _ptr(cache_l), _ptr(a_full), _ptr(l_full), _ptr(ws),
+                                   0 if ws is None else ws.numel() * ws.element_size(),
+                                   None if trace is None else C.byref(trace), _stream(stream)),
+           "fb_residual_step")

@@ -549,3 +549,149 @@ fb_status losa_step(const losa_shape* ls, const void* q_cur, const void* q_prev,
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------------------
+// FlashBlock with a cached sparse residual
+// ---------------------------------------------------------------------------------------
+namespace {
+
+fb_status check_residual(const fb_residual_shape* rs) {
+  if (!rs) return FB_ERR_INVALID_ARG;
+  fb_status st = check_shape(&rs->s);
+  if (st != FB_OK) return st;
+  if (rs->page_size < 1 || rs->max_pages < 1 || rs->max_sel < 1 || rs->max_sel > rs->max_pages)
+    return FB_ERR_INVALID_ARG;
+  if (rs->max_pages > kResidualMaxPages) return FB_ERR_UNSUPPORTED;
+  if (cdiv(max_prefix(&rs->s), rs->page_size) > rs->max_pages) return FB_ERR_INVALID_ARG;
+  if ((int64_t)rs->max_pages * rs->page_size > INT32_MAX) return FB_ERR_UNSUPPORTED;   // 32-bit key indices
+  return FB_OK;
+}
+
+// Sources of one step: the selected pages (0) and the complement pages (1) in one launch,
+// the block in a second one.  Both page sources cover every row of the block.
+struct ResidualPlan {
+  RowPlan rp;
+  SplitPlan sel, comp, blk;
+  Region rsel, rcomp, rblk;
+  size_t pages_off, count_off, ws_bytes;
+};
+ResidualPlan residual_plan(const fb_residual_shape* rs) {
+  ResidualPlan p;
+  const fb_shape* s = &rs->s;
+  const int64_t prefix_pages = cdiv(max_prefix(s), rs->page_size);
+  p.rp = row_plan(s, s->block);
+  p.blk = split_plan(s, p.rp, s->block, fa_rows(s, p.rp) ? 1 : 0);
+  p.sel = split_plan(s, p.rp, std::min<int64_t>(rs->max_sel, prefix_pages) * rs->page_size, s->num_splits);
+  p.comp = split_plan(s, p.rp, prefix_pages * rs->page_size, s->num_splits);
+  p.rsel = partial_region(s, p.rp, p.sel, 0);
+  p.rcomp = partial_region(s, p.rp, p.comp, p.rsel.bytes);
+  p.rblk = partial_region(s, p.rp, p.blk, p.rsel.bytes + p.rcomp.bytes);
+  const size_t groups = (size_t)s->batch * s->h_kv;
+  p.pages_off = p.rsel.bytes + p.rcomp.bytes + p.rblk.bytes;
+  p.count_off = align256(p.pages_off + groups * rs->max_pages * sizeof(int32_t));
+  p.ws_bytes = align256(p.count_off + groups * sizeof(int32_t));
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fb_residual_workspace_size(const fb_residual_shape* rs) {
+  if (check_residual(rs) != FB_OK) return 0;
+  return residual_plan(rs).ws_bytes;
+}
+
+fb_status fb_residual_step(const fb_residual_shape* rs, const void* q, const void* k, const void* v,
+                           const void* k_blk, const void* v_blk, const int32_t* sel_pages,
+                           const int32_t* sel_count, const uint8_t* reuse_mask, float* cache_a, float* cache_l,
+                           void* a_full, float* l_full, void* ws, size_t ws_bytes, const fb_trace* trace,
+                           hipStream_t stream) {
+  fb_status st = check_residual(rs);
+  if (st != FB_OK) return st;
+  const fb_shape* s = &rs->s;
+  if ((st = check_inputs(s, q, k, v)) != FB_OK) return st;
+  if (!k_blk || !v_blk || !aligned16(k_blk) || !aligned16(v_blk)) return FB_ERR_INVALID_ARG;
+  if (!sel_pages || !sel_count || !cache_a || !cache_l || !a_full) return FB_ERR_INVALID_ARG;
+  const ResidualPlan p = residual_plan(rs);
+  if (ws_bytes < p.ws_bytes || !ws || !aligned16(ws)) return FB_ERR_WORKSPACE;
+  int32_t* comp_pages = (int32_t*)((char*)ws + p.pages_off);
+  int32_t* comp_count = (int32_t*)((char*)ws + p.count_off);
+
+  ResidualArgs r;
+  r.batch = s->batch;
+  r.h_q = s->h_q;
+  r.h_kv = s->h_kv;
+  r.G = s->h_q / s->h_kv;
+  r.cu = s->cu_seqlens_k;
+  r.n_uniform = s->seqlen_k;
+  r.page_size = rs->page_size;
+  r.max_pages = rs->max_pages;
+  r.max_sel = rs->max_sel;
+  r.sel_pages = sel_pages;
+  r.sel_count = sel_count;
+  r.mask = reuse_mask;
+  r.comp_pages = comp_pages;
+  r.comp_count = comp_count;
+  rec(trace ? trace->select_begin : nullptr, stream);
+  if (hipError_t e = launch_complement(r, stream)) return hip_status(e);
+  rec(trace ? trace->select_end : nullptr, stream);
+
+  AttnArgs a = base_args(s, q);
+  a.src0 = make_src(p.rp, p.sel, k, v, s->cu_seqlens_k, s->seqlen_k, (float*)ws, p.rsel);
+  a.src0.pages = sel_pages;
+  a.src0.page_count = sel_count;
+  a.src0.page_size = rs->page_size;
+  a.src0.max_union = rs->max_sel;
+  a.src1 = make_src(p.rp, p.comp, k, v, s->cu_seqlens_k, s->seqlen_k, (float*)ws, p.rcomp);
+  a.src1.pages = comp_pages;
+  a.src1.page_count = comp_count;
+  a.src1.page_size = rs->page_size;
+  a.src1.max_union = rs->max_pages;
+  a.src1.mask = reuse_mask;
+  AttnArgs ab = base_args(s, q);
+  ab.src1 = make_src(p.rp, p.blk, k_blk, v_blk, nullptr, s->block, (float*)ws, p.rblk);
+  rec(trace ? trace->attn_begin : nullptr, stream);
+  if (hipError_t e = launch_attn(a, s->dtype == FB_BF16, stream)) return hip_status(e);
+  if (hipError_t e = launch_attn(ab, s->dtype == FB_BF16, stream)) return hip_status(e);
+  rec(trace ? trace->attn_end : nullptr, stream);
+
+  CombineArgs c;
+  memset(&c, 0, sizeof(c));
+  c.mode = kModeResidual;
+  c.batch = s->batch;
+  c.B = s->block;
+  c.h_q = s->h_q;
+  c.h_kv = s->h_kv;
+  c.G = s->h_q / s->h_kv;
+  c.d = s->head_dim;
+  c.po = a.src0.po;
+  c.pml = a.src0.pml;
+  c.p_rows = p.rp.rows;
+  c.p_splits = p.sel.splits;
+  c.p_chunk = p.sel.chunk;
+  c.page_count = sel_count;
+  c.page_size = rs->page_size;
+  c.ro = a.src1.po;
+  c.rml = a.src1.pml;
+  c.r_splits = p.comp.splits;
+  c.r_chunk = p.comp.chunk;
+  c.r_page_count = comp_count;
+  c.bo = ab.src1.po;
+  c.bml = ab.src1.pml;
+  c.b_rows = p.rp.rows;
+  c.b_splits = p.blk.splits;
+  c.b_chunk = p.blk.chunk;
+  c.mask = reuse_mask;
+  c.cache_a = cache_a;
+  c.cache_l = cache_l;
+  c.a_full = a_full;
+  c.l_full = l_full;
+  c.out_bf16 = s->dtype == FB_BF16;
+  rec(trace ? trace->merge_begin : nullptr, stream);
+  if (hipError_t e = launch_combine(c, stream)) return hip_status(e);
+  rec(trace ? trace->merge_end : nullptr, stream);
+  return FB_OK;
+}
+
+}  // extern "C"

@@ -366,14 +366,15 @@ hipError_t launch_generic(const AttnArgs& a, bool bf16, hipStream_t st) {
 }  // namespace
 
 // bf16 groups of at most 32 rows go to the streaming kernel (fb_stream.hip), the rest to
-// the LDS-tiled kernel above.  A paged source never shares a streaming launch with the
-// block source.
+// the LDS-tiled kernel above.  A paged source never shares a streaming launch with a
+// contiguous one.
 hipError_t launch_attn(const AttnArgs& a, bool bf16, hipStream_t st) {
   if (bf16) {
     const int rows = a.src0.n_splits ? a.src0.rows : a.src1.rows;
     if (rows >= kFaMinRows && fa_ok(a, a.src0) && fa_ok(a, a.src1)) return launch_fa(a, st);
     const bool s0 = stream_ok(a, a.src0, a.max_seqlen), s1 = stream_ok(a, a.src1, a.max_seqlen);
-    const bool mixed = a.src0.n_splits > 0 && a.src0.pages != nullptr && a.src1.n_splits > 0;
+    const bool mixed = a.src0.n_splits > 0 && a.src1.n_splits > 0 &&
+                       (a.src0.pages != nullptr) != (a.src1.pages != nullptr);
     if (s0 && s1 && !mixed) return launch_stream(a, st);
     if (s0 && a.src0.n_splits > 0) {
       AttnArgs a0 = a;

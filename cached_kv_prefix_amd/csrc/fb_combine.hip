@@ -15,6 +15,14 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs C) {
   row_finish<E, UP, UB>(C, lane, st);
 }
 
+template <int E, int UP, int UR, int UB>
+__global__ void __launch_bounds__(256) combine_residual_kernel(const CombineArgs C) {
+  const int lane = threadIdx.x & 63;
+  const int rowid = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  if (rowid >= C.batch * C.B * C.h_q) return;
+  residual_row<E, UP, UR, UB>(C, rowid, lane);
+}
+
 template <int E>
 __global__ void __launch_bounds__(256) lse_merge_kernel(int64_t rows, int d, const float* ao_, const float* lo_,
                                                         const float* ai_, const float* li_, void* af_,
@@ -93,6 +101,15 @@ hipError_t launch_combine(const CombineArgs& c, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   if (rows > INT32_MAX - 4) return hipErrorInvalidValue;   // row indices are 32-bit
   const dim3 grid((unsigned)((rows + 3) / 4));
+  if (c.mode == kModeResidual) {   // chunk loads issued up front: 4 selected, 4 residual, 1 block
+    if (c.d <= 64)
+      hipLaunchKernelGGL((combine_residual_kernel<1, 4, 4, 1>), grid, dim3(256), 0, st, c);
+    else if (c.d <= 128)
+      hipLaunchKernelGGL((combine_residual_kernel<2, 4, 4, 1>), grid, dim3(256), 0, st, c);
+    else
+      hipLaunchKernelGGL((combine_residual_kernel<4, 4, 4, 1>), grid, dim3(256), 0, st, c);
+    return hipGetLastError();
+  }
   // chunk loads issued up front: as many as the plan has (d = 128), else 8
   const int up = c.p_splits <= 1 ? 1 : c.p_splits <= 2 ? 2 : c.p_splits <= 4 ? 4 : 8;
   const bool ub1 = c.b_splits <= 1;

@@ -9,6 +9,10 @@
 // reuse and recompute on unchanged inputs give bit-identical outputs.
 // LoSA ("LoSA", §2 steps 2 and 4): active rows take the sparse prefix result into the
 // cache; stable rows reuse their cached statistics; every row merges with the block part.
+// Sparse residual ("Resumo Técnico: FlashBlock", §2, Estratégias de Reutilização
+// Adaptativa, "Compatibilidade com Atenção Esparsa"): the selected pages are attended to at every step, the residual over the
+// unselected pages is refreshed into the cache or reused from it, and the three parts are
+// merged in log space.
 #pragma once
 #include "fb_device.hpp"
 #include "fb_internal.hpp"
@@ -268,6 +272,107 @@ __device__ __forceinline__ void row_finish(const CombineArgs& C, int lane, const
     }
   }
   if (C.l_full && lane == 0) C.l_full[st.rowid] = lf;
+}
+
+// Three-way log-space merge of one row (the two-way merge with a third term):
+//   m = max_i L_i, A = sum_i e^{L_i - m} A_i / sum_i e^{L_i - m}, L = m + ln sum_i e^{L_i - m}.
+// Parts with L = -inf weigh nothing; all three empty gives 0 / -inf.
+template <int E>
+__device__ __forceinline__ void merge3_row(const float (&a1)[E], float l1, const float (&a2)[E], float l2,
+                                           const float (&a3)[E], float l3, float (&af)[E], float& lf) {
+  const float m = fmaxf(fmaxf(l1, l2), l3);
+  if (m == kNegInf) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) af[e] = 0.f;
+    lf = kNegInf;
+    return;
+  }
+  const float w1 = l1 == kNegInf ? 0.f : fast_exp2((l1 - m) * kLog2e);
+  const float w2 = l2 == kNegInf ? 0.f : fast_exp2((l2 - m) * kLog2e);
+  const float w3 = l3 == kNegInf ? 0.f : fast_exp2((l3 - m) * kLog2e);
+  const float den = w1 + w2 + w3;
+  const float inv = 1.0f / den;
+#pragma unroll
+  for (int e = 0; e < E; ++e) af[e] = (w1 * a1[e] + w2 * a2[e] + w3 * a3[e]) * inv;
+  lf = m + fast_log2(den) * kLn2;
+}
+
+// One row of the sparse-residual step.  Every partial load (selected pages, complement
+// pages, block) and the cached residual row are issued before the refresh decision is
+// read.  A refreshing row reduces its complement chunks, writes them to the cache and
+// merges the very values it wrote, so refresh and reuse on unchanged inputs give
+// bit-identical outputs.
+template <int E, int UP, int UR, int UB>
+__device__ __forceinline__ void residual_row(const CombineArgs& C, int rowid, int lane) {
+  const int h = rowid % C.h_q;
+  const int i = (rowid / C.h_q) % C.B;
+  const int b = rowid / (C.h_q * C.B);
+  const int hk = h / C.G, jg = h % C.G;
+  const int d = C.d;
+  const int64_t roff = (int64_t)rowid * d;
+  const int prow = jg * C.B + i;
+  const int64_t grp = (int64_t)b * C.h_kv + hk;
+
+  RowPartials<E, UP> PS;
+  RowPartials<E, UR> PR;
+  RowPartials<E, UB> PB;
+  const int64_t sslot0 = grp * C.p_splits, rslot0 = grp * C.r_splits, bslot0 = grp * C.b_splits;
+  if (C.p_splits > 0) issue_partials<E, UP>(C.po, C.pml, sslot0, C.p_rows, prow, C.p_splits, d, lane, PS);
+  if (C.r_splits > 0) issue_partials<E, UR>(C.ro, C.rml, rslot0, C.p_rows, prow, C.r_splits, d, lane, PR);
+  if (C.b_splits > 0) issue_partials<E, UB>(C.bo, C.bml, bslot0, C.b_rows, prow, C.b_splits, d, lane, PB);
+  float cached[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int dd = lane + 64 * e;
+    cached[e] = dd < d ? C.cache_a[roff + dd] : 0.f;
+  }
+  const float cached_l = C.cache_l[rowid];
+  const bool fresh = C.mask ? C.mask[b * C.h_q + h] == 0 : true;
+  const int ns = C.page_count[grp] * C.page_size;
+
+  float as[E], ar[E], ai[E], af[E];
+  float ls, lr, li, lf;
+  {
+    const int n = C.p_splits > 0 ? min(n_chunks(ns, C.p_chunk), C.p_splits) : 0;
+    reduce_chunks<E, UP>(PS, C.po, C.pml, sslot0, C.p_rows, prow, n, d, lane, as, ls);
+  }
+  if (fresh) {
+    const int nr = C.r_page_count[grp] * C.page_size;
+    const int n = C.r_splits > 0 ? min(n_chunks(nr, C.r_chunk), C.r_splits) : 0;
+    reduce_chunks<E, UR>(PR, C.ro, C.rml, rslot0, C.p_rows, prow, n, d, lane, ar, lr);
+    float* ca = C.cache_a + roff;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int dd = lane + 64 * e;
+      if (dd < d) ca[dd] = ar[e];
+    }
+    if (lane == 0) C.cache_l[rowid] = lr;
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) ar[e] = cached[e];
+    lr = cached_l;
+  }
+  {
+    const int n = C.b_splits > 0 ? min(n_chunks(C.B, C.b_chunk), C.b_splits) : 0;
+    reduce_chunks<E, UB>(PB, C.bo, C.bml, bslot0, C.b_rows, prow, n, d, lane, ai, li);
+  }
+  merge3_row<E>(as, ls, ar, lr, ai, li, af, lf);
+  if (C.out_bf16) {
+    uint16_t* out = (uint16_t*)C.a_full + roff;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int dd = lane + 64 * e;
+      if (dd < d) out[dd] = f32_to_bf16(af[e]);
+    }
+  } else {
+    float* out = (float*)C.a_full + roff;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int dd = lane + 64 * e;
+      if (dd < d) out[dd] = af[e];
+    }
+  }
+  if (C.l_full && lane == 0) C.l_full[rowid] = lf;
 }
 
 }  // namespace fb

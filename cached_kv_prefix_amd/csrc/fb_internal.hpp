@@ -35,7 +35,7 @@ struct AttnSrc {
   float* pml;                 // partial m,l [batch][h_kv][n_splits][rows][2]
 };
 
-enum CombineMode { kModeStep = 0, kModePrefixOnly = 1, kModeBlockOnly = 2, kModeLosa = 3 };
+enum CombineMode { kModeStep = 0, kModePrefixOnly = 1, kModeBlockOnly = 2, kModeLosa = 3, kModeResidual = 4 };
 
 struct CombineArgs {
   int32_t mode;
@@ -49,6 +49,10 @@ struct CombineArgs {
   const uint8_t* mask;                 // step: [batch][h_q], null = recompute all
   const int32_t* m_upd; int32_t tau;   // step: threshold rule evaluated in place of mask
   const int32_t* active; int32_t n_active;   // LoSA
+  // residual mode: the prefix partials are the selected pages (page_count); these are the
+  // complement pages' partials (page counts r_page_count), which refresh the cache
+  const float* ro; const float* rml; int32_t r_splits; int32_t r_chunk;
+  const int32_t* r_page_count;
   float* cache_a; float* cache_l;      // step/LoSA cache, or prefix-only outputs
   float* ain; float* lin;              // block-only outputs
   void* a_full; int32_t out_bf16; float* l_full;
@@ -118,5 +122,19 @@ hipError_t launch_topk(const LosaArgs& a, const double* scores, int32_t* topk_pa
                        hipStream_t st);
 hipError_t launch_union(const LosaArgs& a, const int32_t* topk_pages, int32_t* union_pages,
                         int32_t* union_count, hipStream_t st);
+
+
+// FlashBlock with a cached sparse residual: the complement of each (sequence, KV head)
+// page selection, for the groups where some query head refreshes the residual.
+struct ResidualArgs {
+  int32_t batch, h_q, h_kv, G;
+  const int32_t* cu; int32_t n_uniform;
+  int32_t page_size, max_pages, max_sel;
+  const int32_t* sel_pages; const int32_t* sel_count;   // [batch][h_kv][max_sel], [batch][h_kv]
+  const uint8_t* mask;                                  // [batch][h_q] or null (all refresh)
+  int32_t* comp_pages; int32_t* comp_count;             // [batch][h_kv][max_pages], [batch][h_kv]
+};
+constexpr int kResidualMaxPages = 65536;
+hipError_t launch_complement(const ResidualArgs& r, hipStream_t st);
 
 }  // namespace fb

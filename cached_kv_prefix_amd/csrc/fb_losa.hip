@@ -40,24 +40,6 @@ __device__ __forceinline__ uint64_t order_key(double s) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-// Inclusive scan of one value per thread over a 256-thread block: a shuffle scan inside
-// each wave, then the wave totals through LDS (tmp holds 4 ints).  Every thread gets its
-// inclusive prefix; *total receives the block sum.
-__device__ __forceinline__ int block_incl_scan(int v, int* tmp, int* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(v, o);
-    if (lane >= o) v += u;
-  }
-  if (lane == 63) tmp[w] = v;
-  __syncthreads();
-  int before = 0;
-  for (int i = 0; i < w; ++i) before += tmp[i];
-  *total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
-  __syncthreads();
-  return v + before;
-}
 
 }  // namespace
 

@@ -343,8 +343,10 @@ hipError_t launch_stream(const AttnArgs& a, hipStream_t st) {
   const int gy = a.src0.n_splits + a.src1.n_splits;
   if (gy == 0) return hipSuccess;
   dim3 grid(a.h_kv, gy, a.batch);
-  const bool paged = a.src0.n_splits && a.src0.pages != nullptr;   // only the LoSA sparse source is paged
-  if (paged && a.src1.n_splits) return hipErrorInvalidValue;
+  // both sources of a launch are paged (selected / complement pages) or neither is
+  const bool paged = (a.src0.n_splits ? a.src0.pages : a.src1.pages) != nullptr;
+  if (a.src0.n_splits && a.src1.n_splits && (a.src0.pages != nullptr) != (a.src1.pages != nullptr))
+    return hipErrorInvalidValue;
   if (paged) {
     hipLaunchKernelGGL((attn_stream_kernel<kStreamDepth, kStreamTmax, true>), grid, dim3(256), 0, st, a);
   } else if (FB_STREAM_SRC1_FIRST && a.src1.n_splits) {

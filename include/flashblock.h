@@ -8,8 +8,11 @@
  *            log-space merge A_full = (e^{L_out-m} A_out + e^{L_in-m} A_in) /
  *            (e^{L_out-m} + e^{L_in-m}), m = max(L_out, L_in)); "Estratégias de
  *            Reutilização Adaptativa" (threshold rule M < tau; per-head rule sim > gamma).
+ *            "Compatibilidade com Atenção Esparsa" (unselected keys as the block-external
+ *            set, their residual contribution cached).
  *   [FB-abs] "FlashBlock: Attention Caching for Efficient Long-Context Block Diffusion",
- *            abstract: block-wise causal inference over a growing KV cache.
+ *            abstract: block-wise causal inference over a growing KV cache; FlashBlock as
+ *            a complementary residual reuse strategy under sparse attention.
  *   [LoSA]   "LoSA: Locality Aware Sparse Attention for Block-Wise Diffusion Language
  *            Models" (gist.science, Spanish), §1 (KV inflation: cost is the size of the
  *            union of the queries' selections) and §2 "El Algoritmo LoSA" steps 1-4.
@@ -85,7 +88,7 @@ typedef struct fb_shape {
 typedef struct fb_trace {
   hipEvent_t attn_begin, attn_end;    /* the attention kernel (prefix and block passes)  */
   hipEvent_t merge_begin, merge_end;  /* the split-reduction / merge / cache kernel      */
-  hipEvent_t select_begin, select_end;/* LoSA: the selection kernels (scores, top-k, union) */
+  hipEvent_t select_begin, select_end;/* LoSA selection (scores, top-k, union); residual: complement */
 } fb_trace;
 
 const char* fb_status_string(fb_status s);
@@ -221,6 +224,44 @@ fb_status losa_step(const losa_shape* ls, const void* q_cur, const void* q_prev,
                     void* a_full, float* l_full, int32_t* active, int32_t* topk_pages,
                     int32_t* union_pages, int32_t* union_count, void* ws, size_t ws_bytes,
                     const fb_trace* trace, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------
+ * FlashBlock with a cached sparse residual [FB-pt §2, Estratégias de Reutilização
+ * Adaptativa, "Compatibilidade com Atenção Esparsa"; FB-abs: a complementary residual
+ * reuse strategy for sparse attention]: the prefix keys that a sparse selection leaves
+ * out are treated as the block-external set, and their attention (the residual) is cached.
+ * ------------------------------------------------------------------------------------ */
+typedef struct fb_residual_shape {
+  fb_shape s;          /* B, heads, prefix lengths, dtype                                 */
+  int32_t page_size;   /* tokens per page (>= 1); page p holds tokens p*P .. p*P + P - 1  */
+  int32_t max_pages;   /* >= ceil(N_b / page_size) for every b; <= 65536                  */
+  int32_t max_sel;     /* capacity of sel_pages per (b, kv head), 1 <= max_sel <= max_pages */
+} fb_residual_shape;
+
+/* Workspace bytes for fb_residual_step (partials of the three passes and the complement
+ * page lists).  0 on an invalid shape. */
+size_t fb_residual_workspace_size(const fb_residual_shape* rs);
+
+/* One step with a cached residual.  Selection S[b][g] = sel_pages[b][g][0 .. sel_count[b][g]),
+ * distinct page indices below ceil(N_b / page_size), any order (for example the
+ * losa_select_union output, with max_sel = losa_union_capacity); sel_count in [0, max_sel].
+ *   every row, every step: (A_s, L_s) = attention over the tokens of S of its KV head;
+ *   rows of heads with reuse_mask[b][h] == 0 (refresh): (A_r, L_r) = attention over the
+ *     prefix tokens outside S, written to cache_a / cache_l;
+ *   rows of heads with reuse_mask[b][h] == 1 (reuse): the pages outside S are not read;
+ *     (A_r, L_r) = the cache rows, left untouched;
+ *   every row: (A_in, L_in) over the block, then the three-way log-space merge
+ *     m = max(L_s, L_r, L_in), a_full = sum_i e^{L_i-m} A_i / sum_i e^{L_i-m},
+ *     l_full = m + log sum_i e^{L_i-m} (optional output).
+ * Tokens >= N_b do not exist (the tail page is partial).  A refresh step attends to every
+ * prefix token exactly once, so it equals full attention over prefix and block.  The first
+ * step must refresh every head.  reuse_mask may be NULL (refresh every head).  With
+ * identical inputs and cache, reuse and refresh give bit-identical a_full. */
+fb_status fb_residual_step(const fb_residual_shape* rs, const void* q, const void* k, const void* v,
+                           const void* k_blk, const void* v_blk, const int32_t* sel_pages,
+                           const int32_t* sel_count, const uint8_t* reuse_mask, float* cache_a,
+                           float* cache_l, void* a_full, float* l_full, void* ws, size_t ws_bytes,
+                           const fb_trace* trace, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-SEED_TINY, SEED_DLLM, SEED_RAGGED, SEED_VIDEO, SEED_LOSA = 0, 1, 2, 3, 4
+SEED_TINY, SEED_DLLM, SEED_RAGGED, SEED_VIDEO, SEED_LOSA, SEED_RESIDUAL = 0, 1, 2, 3, 4, 5
 
 
 def rng(seed: int) -> np.random.Generator:
@@ -172,3 +172,46 @@ def custom(seed, batch, h_q, h_kv, d, B, seqlens, dtype="bf16", std=1.0) -> Prob
     p = make_problem("custom", seed, batch, h_q, h_kv, d, B, seqlens, dtype=dtype, std=std)
     p.extra.pop("gen")
     return p
+
+
+def page_selection(seed, seqlens, h_kv, page, n_sel, kinds=("random",)) -> list:
+    """Per (sequence, KV head) a set of distinct prefix pages (page = ``page`` consecutive
+    tokens), ascending.  Group j of the flattened (sequence, KV head) order takes kind
+    ``kinds[j % len(kinds)]``: "empty"; "all" (every page); "random" (min(n_sel, pages)
+    pages drawn without replacement); "tail" (as random, with the partial last page in)."""
+    g = rng(seed)
+    out, j = [], 0
+    for n in np.asarray(seqlens, dtype=np.int64):
+        P = int(-(-int(n) // page))
+        row = []
+        for _ in range(h_kv):
+            kind = kinds[j % len(kinds)]
+            j += 1
+            if kind == "empty" or P == 0:
+                row.append(np.zeros(0, np.int64))
+            elif kind == "all":
+                row.append(np.arange(P, dtype=np.int64))
+            else:
+                s = g.permutation(P)[:min(n_sel, P)]
+                if kind == "tail" and P - 1 not in s:
+                    s[-1] = P - 1
+                row.append(np.sort(s).astype(np.int64))
+        out.append(row)
+    return out
+
+
+def pack_selection(sel, max_sel, shuffle_seed=None):
+    """[batch][h_kv][max_sel] int32 page lists padded with -1, and [batch][h_kv] counts.
+    With ``shuffle_seed`` each list is permuted (the selection is a set; order is free)."""
+    b, hk = len(sel), len(sel[0])
+    pages = np.full((b, hk, max_sel), -1, dtype=np.int32)
+    count = np.zeros((b, hk), dtype=np.int32)
+    g = None if shuffle_seed is None else rng(shuffle_seed)
+    for i in range(b):
+        for h in range(hk):
+            s = np.asarray(sel[i][h], dtype=np.int32)
+            if g is not None:
+                s = g.permutation(s)
+            pages[i, h, :len(s)] = s
+            count[i, h] = len(s)
+    return pages, count

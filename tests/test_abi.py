@@ -147,3 +147,36 @@ def test_mask_validation():
     assert lib.fb_mask_similarity(None, 0.95, 0, None, None) == 0
     assert lib.fb_mask_similarity(None, 0.95, 4, None, None) == 1
     assert lib.fb_head_cosine(0, 32, 32, 128, None, None, None, None) == 1
+
+
+def residual_shape(**kw):
+    s = dllm_shape(block=64, seqlen_k=131072)
+    base = dict(page_size=16, max_sel=512)
+    base.update(kw)
+    return fb.make_residual_shape(s, **base)
+
+
+def test_residual_sizes_and_shape_checks():
+    rs = residual_shape()
+    assert rs.max_pages == 8192
+    w = fb.residual_workspace_size(rs)
+    assert w == fb.residual_workspace_size(residual_shape()) and w >= 32 * 8192 * 4   # complement lists
+    assert fb.residual_workspace_size(residual_shape(max_sel=0)) == 0
+    assert fb.residual_workspace_size(residual_shape(max_sel=9000)) == 0            # > max_pages
+    assert fb.residual_workspace_size(residual_shape(max_pages=100)) == 0           # prefix needs 8192
+    assert fb.residual_workspace_size(residual_shape(max_pages=70000, max_sel=10)) == 0   # above 65536
+    assert fb.residual_workspace_size(residual_shape(page_size=0, max_pages=1, max_sel=1)) == 0
+
+
+def test_residual_step_rejects_bad_args_before_launch():
+    lib = fb.load()
+    rs = residual_shape()
+    f = C.c_void_p(0x10000)
+    n = fb.residual_workspace_size(rs)
+    call = lambda sp=f, sc=f, ws=f, nb=n, q=f: lib.fb_residual_step(C.byref(rs), q, f, f, f, f, sp, sc, None, f, f, f,
+                                                                   None, ws, nb, None, None)
+    assert call(sp=None) == 1 and call(sc=None) == 1 and call(q=None) == 1
+    assert call(q=C.c_void_p(0x10002)) == 1
+    assert call(nb=n - 1) == 3 and call(ws=None) == 3
+    bad = residual_shape(max_sel=0)
+    assert lib.fb_residual_step(C.byref(bad), f, f, f, f, f, f, f, None, f, f, f, None, f, n, None, None) == 1
