@@ -134,6 +134,31 @@ def time_steps(fn, steps, warmup):
     return wall, float(np.mean(kern)) / 1e3, kern
 
 
+def graph_step_time(fn, steps, warmup=3):
+    """One call of fn captured into a HIP graph (stream capture through torch.cuda.CUDAGraph),
+    then `steps` replays back to back: the step time without the host's per-launch cost.
+    The step itself enqueues no memset, so the graph holds kernel nodes only."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(None)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn(None)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    del g
+    return wall
+
+
 def flushed_step_times(fn, n=10):
     """Per-step event timing after a 1 GiB read before each step (outside the events), so
     the 256 MB last-level cache holds none of the inputs.  A read, not a write: dirty
@@ -154,7 +179,7 @@ def flushed_step_times(fn, n=10):
     return float(np.median(out))
 
 
-STREAM_KERNEL = "fb::attn_stream_kernel<1, 40, false, 1>"
+STREAM_KERNEL = "fb::attn_stream_kernel<1, 40, false>"
 
 
 def kernel_source_sha():
@@ -260,6 +285,10 @@ def main():
         one = torch.zeros_like(m_fresh)
         wall_r, _, _ = time_steps(lambda tr: run_step(fb, shape, dev, bufs, one, trace=tr), args.steps, 3)
         extra["reuse_step_us"] = wall_r * 1e6
+        extra["reuse_step_graph_us"] = graph_step_time(lambda tr: run_step(fb, shape, dev, bufs, one, trace=tr),
+                                                       args.steps) * 1e6
+        extra["fresh_step_graph_us"] = graph_step_time(lambda tr: run_step(fb, shape, dev, bufs, m_fresh, trace=tr),
+                                                       args.steps) * 1e6
         # an 8-step block with the drawn M (tau 4): mean step time
         def block(tr):
             for s in range(8):
@@ -401,7 +430,41 @@ def other_workloads(fb, args):
                           "union_pages_mean": float(cnt.mean()), "density": float(cnt.mean()) / ls.max_pages,
                           "alg_bytes": meta_bytes + union_bytes,
                           "frac_hbm_step": (meta_bytes + union_bytes) / w_s / 1e9 / HBM_PEAK_GBS}
+    out["sparse_residual"] = residual_workload(fb, p, dev, shape, sel, cap, steps)
     return out
+
+
+def residual_workload(fb, p, dev, shape, sel, cap, steps):
+    """FlashBlock with a cached sparse residual on the LoSA workload's shape: the selection
+    is the union the LoSA selection just produced (per KV head, about 500 of 8192 pages).
+    A refresh step attends to the selection and to its complement (the whole prefix) and
+    caches the residual; a reuse step reads the selected pages only."""
+    import torch
+    rs = fb.make_residual_shape(shape, page_size=16, max_sel=cap)
+    b, B, h, d = p.q.shape
+    bufs = dict(ws=torch.empty(fb.residual_workspace_size(rs), dtype=torch.uint8, device="cuda"),
+                ca=torch.zeros((b, B, h, d), device="cuda"), cl=torch.zeros((b, B, h), device="cuda"),
+                af=torch.zeros((b, B, h, d), dtype=torch.bfloat16, device="cuda"),
+                lf=torch.zeros((b, B, h), device="cuda"))
+    ones = torch.ones((b, h), dtype=torch.uint8, device="cuda")
+
+    def step(mask):
+        return lambda tr: fb.residual_step(rs, dev["q"], dev["k"], dev["v"], dev["k_blk"], dev["v_blk"], sel["union"],
+                                           sel["count"], mask, bufs["ca"], bufs["cl"], bufs["af"], bufs["lf"],
+                                           bufs["ws"], trace=tr)
+    w_f, a_f, _ = time_steps(step(None), steps, 2)
+    w_r, a_r, _ = time_steps(step(ones), steps, 2)
+    g_f = graph_step_time(step(None), steps)
+    g_r = graph_step_time(step(ones), steps)
+    cnt = sel["count"].cpu().numpy()
+    sel_bytes = float(np.minimum(cnt * 16, p.seqlens[0]).sum()) * d * 2 * 2
+    all_bytes = float(p.seqlens[0]) * p.h_kv * d * 2 * 2
+    return {"refresh_step_us": w_f * 1e6, "refresh_attn_us": a_f * 1e6, "refresh_kv_GBps": all_bytes / w_f / 1e9,
+            "refresh_attn_frac_hbm": all_bytes / a_f / 1e9 / HBM_PEAK_GBS,
+            "reuse_step_us": w_r * 1e6, "reuse_attn_us": a_r * 1e6, "reuse_kv_GBps": sel_bytes / w_r / 1e9,
+            "reuse_attn_frac_hbm": sel_bytes / a_r / 1e9 / HBM_PEAK_GBS,
+            "refresh_step_graph_us": g_f * 1e6, "reuse_step_graph_us": g_r * 1e6,
+            "selected_pages_mean": float(cnt.mean()), "selected_kv_bytes": sel_bytes, "prefix_kv_bytes": all_bytes}
 
 
 if __name__ == "__main__":

@@ -365,27 +365,26 @@ hipError_t launch_generic(const AttnArgs& a, bool bf16, hipStream_t st) {
 }
 }  // namespace
 
-// bf16 groups of at most 32 rows go to the streaming kernel (fb_stream.hip), the rest to
-// the LDS-tiled kernel above.  A paged source never shares a streaming launch with a
-// contiguous one.
+// bf16 groups of more than 32 rows go to the query-tiled kernel (fb_fa.hip), groups of at
+// most 32 rows to the streaming kernel (fb_stream.hip), the rest to the LDS-tiled kernel
+// above.  A launch whose sources differ in kind (paged / contiguous) is split into one
+// launch per source.
 hipError_t launch_attn(const AttnArgs& a, bool bf16, hipStream_t st) {
+  const bool mixed = a.src0.n_splits > 0 && a.src1.n_splits > 0 &&
+                     (a.src0.pages != nullptr) != (a.src1.pages != nullptr);
+  if (mixed) {
+    AttnArgs a0 = a, a1 = a;
+    a0.src1.n_splits = 0;
+    a0.src1.qgroups = 0;
+    a1.src0.n_splits = 0;
+    a1.src0.qgroups = 0;
+    if (hipError_t e = launch_attn(a0, bf16, st)) return e;
+    return launch_attn(a1, bf16, st);
+  }
   if (bf16) {
     const int rows = a.src0.n_splits ? a.src0.rows : a.src1.rows;
     if (rows >= kFaMinRows && fa_ok(a, a.src0) && fa_ok(a, a.src1)) return launch_fa(a, st);
-    const bool s0 = stream_ok(a, a.src0, a.max_seqlen), s1 = stream_ok(a, a.src1, a.max_seqlen);
-    const bool mixed = a.src0.n_splits > 0 && a.src1.n_splits > 0 &&
-                       (a.src0.pages != nullptr) != (a.src1.pages != nullptr);
-    if (s0 && s1 && !mixed) return launch_stream(a, st);
-    if (s0 && a.src0.n_splits > 0) {
-      AttnArgs a0 = a;
-      a0.src1.n_splits = 0;
-      if (hipError_t e = launch_stream(a0, st)) return e;
-      AttnArgs a1 = a;
-      a1.src0.n_splits = 0;
-      a1.src0.qgroups = 0;
-      if (a1.src1.rows >= kFaMinRows && fa_ok(a1, a1.src1)) return launch_fa(a1, st);
-      return launch_generic(a1, bf16, st);
-    }
+    if (stream_ok(a, a.src0, a.max_seqlen) && stream_ok(a, a.src1, a.max_seqlen)) return launch_stream(a, st);
   }
   return launch_generic(a, bf16, st);
 }

@@ -101,13 +101,13 @@ hipError_t launch_combine(const CombineArgs& c, hipStream_t st) {
   if (rows == 0) return hipSuccess;
   if (rows > INT32_MAX - 4) return hipErrorInvalidValue;   // row indices are 32-bit
   const dim3 grid((unsigned)((rows + 3) / 4));
-  if (c.mode == kModeResidual) {   // chunk loads issued up front: 4 selected, 4 residual, 1 block
+  if (c.mode == kModeResidual) {   // chunk loads issued at once: up to 16 selected, 32 residual, 1 block
     if (c.d <= 64)
-      hipLaunchKernelGGL((combine_residual_kernel<1, 4, 4, 1>), grid, dim3(256), 0, st, c);
+      hipLaunchKernelGGL((combine_residual_kernel<1, 16, 32, 1>), grid, dim3(256), 0, st, c);
     else if (c.d <= 128)
-      hipLaunchKernelGGL((combine_residual_kernel<2, 4, 4, 1>), grid, dim3(256), 0, st, c);
+      hipLaunchKernelGGL((combine_residual_kernel<2, 16, 32, 1>), grid, dim3(256), 0, st, c);
     else
-      hipLaunchKernelGGL((combine_residual_kernel<4, 4, 4, 1>), grid, dim3(256), 0, st, c);
+      hipLaunchKernelGGL((combine_residual_kernel<4, 8, 8, 1>), grid, dim3(256), 0, st, c);
     return hipGetLastError();
   }
   // chunk loads issued up front: as many as the plan has (d = 128), else 8

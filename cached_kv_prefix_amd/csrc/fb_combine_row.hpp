@@ -297,11 +297,33 @@ __device__ __forceinline__ void merge3_row(const float (&a1)[E], float l1, const
   lf = m + fast_log2(den) * kLn2;
 }
 
-// One row of the sparse-residual step.  Every partial load (selected pages, complement
-// pages, block) and the cached residual row are issued before the refresh decision is
-// read.  A refreshing row reduces its complement chunks, writes them to the cache and
-// merges the very values it wrote, so refresh and reuse on unchanged inputs give
-// bit-identical outputs.
+// Loads of the first min(nmax, U) chunks of one row, each behind a uniform guard (no
+// redundant loads when the plan has fewer chunks than U).
+template <int E, int U>
+__device__ __forceinline__ void issue_partials_guarded(const float* po, const float* pml, int64_t slot0, int rows,
+                                                       int row, int nmax, int d, int lane, RowPartials<E, U>& P) {
+  const int sl = lane < nmax ? lane : 0;
+  const float* ml = pml + ((slot0 + sl) * rows + row) * 2;
+  P.m = ml[0];
+  P.l = ml[1];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (u < nmax) {
+      const int64_t r = (slot0 + u) * rows + row;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int dd = lane + 64 * e;
+        P.x[u][e] = dd < d ? po[r * d + dd] : 0.f;
+      }
+    }
+  }
+}
+
+// One row of the sparse-residual step.  The selected-page and block partials and the
+// cached residual row are loaded before the refresh flag is known; the complement
+// partials, which only a refreshing row uses, after it.  A refreshing row reduces its
+// complement chunks, writes them to the cache and merges the very values it wrote, so
+// refresh and reuse on unchanged inputs give bit-identical outputs.
 template <int E, int UP, int UR, int UB>
 __device__ __forceinline__ void residual_row(const CombineArgs& C, int rowid, int lane) {
   const int h = rowid % C.h_q;
@@ -317,9 +339,8 @@ __device__ __forceinline__ void residual_row(const CombineArgs& C, int rowid, in
   RowPartials<E, UR> PR;
   RowPartials<E, UB> PB;
   const int64_t sslot0 = grp * C.p_splits, rslot0 = grp * C.r_splits, bslot0 = grp * C.b_splits;
-  if (C.p_splits > 0) issue_partials<E, UP>(C.po, C.pml, sslot0, C.p_rows, prow, C.p_splits, d, lane, PS);
-  if (C.r_splits > 0) issue_partials<E, UR>(C.ro, C.rml, rslot0, C.p_rows, prow, C.r_splits, d, lane, PR);
-  if (C.b_splits > 0) issue_partials<E, UB>(C.bo, C.bml, bslot0, C.b_rows, prow, C.b_splits, d, lane, PB);
+  if (C.p_splits > 0) issue_partials_guarded<E, UP>(C.po, C.pml, sslot0, C.p_rows, prow, C.p_splits, d, lane, PS);
+  if (C.b_splits > 0) issue_partials_guarded<E, UB>(C.bo, C.bml, bslot0, C.b_rows, prow, C.b_splits, d, lane, PB);
   float cached[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -329,6 +350,8 @@ __device__ __forceinline__ void residual_row(const CombineArgs& C, int rowid, in
   const float cached_l = C.cache_l[rowid];
   const bool fresh = C.mask ? C.mask[b * C.h_q + h] == 0 : true;
   const int ns = C.page_count[grp] * C.page_size;
+  if (fresh && C.r_splits > 0)
+    issue_partials_guarded<E, UR>(C.ro, C.rml, rslot0, C.p_rows, prow, C.r_splits, d, lane, PR);
 
   float as[E], ar[E], ai[E], af[E];
   float ls, lr, li, lf;

@@ -51,12 +51,14 @@ __device__ __forceinline__ int fa_qtiles(const AttnSrc& S, int rows_per_wg) {
   return (S.rows + rows_per_wg - 1) / rows_per_wg;
 }
 
-template <int QT, int W, bool DEEP>
+template <int QT, int W, bool DEEP, bool PAGED>
 __global__ void __launch_bounds__(64 * W, QT == 1 && W == 4 ? 2 : 1) attn_fa_kernel(const AttnArgs A) {
   constexpr int D = 128;
   constexpr int ROWS_WG = 32 * W * QT;
   constexpr int NP = 16 / W;                    // 16-byte pieces per thread per K (or V) tile
+  static_assert(!PAGED || DEEP, "paged sources run on the deep-prefetch variant");
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][2 * kFaTileBytes];   // [buf][K | V]
+  __shared__ int32_t pl_lds[PAGED ? kFaMaxChunkPages : 1];                         // the chunk's pages
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -111,10 +113,32 @@ __global__ void __launch_bounds__(64 * W, QT == 1 && W == 4 ? 2 : 1) attn_fa_ker
   }
 
   // ---- K / V tiles: thread piece u = row (tid >> 4) + 16 u, 16-byte chunk tid & 15 ------
+  // Contiguous source: the buffer resources start at the chunk, and rows past the chunk
+  // end read as zero.  Paged source (power-of-two page size 2^sh): they start at the
+  // sequence, key `key` of the chunk is token pages[key >> sh] * 2^sh + (key & (2^sh - 1)),
+  // and a key past the chunk end or a token past the sequence end is given the offset
+  // nrec, which reads as zero; such keys are masked out of the softmax by the tile's
+  // validity mask.
   const int64_t tstride = (int64_t)A.h_kv * D;
-  const uint16_t* kbase = (const uint16_t*)S.k + ((int64_t)si.seq0 + kbeg) * tstride + hk * D;
-  const uint16_t* vbase = (const uint16_t*)S.v + ((int64_t)si.seq0 + kbeg) * tstride + hk * D;
-  const int nrec = (kend - kbeg) * (int)tstride * 2;   // rows past the chunk read as zero
+  const int tok0 = PAGED ? 0 : kbeg;
+  const uint16_t* kbase = (const uint16_t*)S.k + ((int64_t)si.seq0 + tok0) * tstride + hk * D;
+  const uint16_t* vbase = (const uint16_t*)S.v + ((int64_t)si.seq0 + tok0) * tstride + hk * D;
+  const int nrec = ((PAGED ? si.n_seq : kend) - tok0) * (int)tstride * 2;
+  int sh = 0, pbase = 0, npl = 1;
+  if constexpr (PAGED) {
+    sh = __builtin_ctz(S.page_size);
+    pbase = kbeg >> sh;
+    npl = ((kend - 1) >> sh) - pbase + 1;
+    const int32_t* pg = S.pages + (int64_t)(b * A.h_kv + hk) * S.max_union + pbase;
+    for (int i = tid; i < npl; i += 64 * W) pl_lds[i] = pg[i];
+    __syncthreads();
+  }
+  const int pmask = (1 << sh) - 1;
+  // Token of chunk key `key` >= kbeg, branch-free: keys past the chunk end read the last
+  // staged page (the caller discards them).
+  auto paged_tok = [&](int key) -> int {
+    return (pl_lds[min((key >> sh) - pbase, npl - 1)] << sh) + (key & pmask);
+  };
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, nrec, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, nrec, 0x00020000);
   const int p_row = tid >> 4, p_chunk = tid & 15;
@@ -129,15 +153,26 @@ __global__ void __launch_bounds__(64 * W, QT == 1 && W == 4 ? 2 : 1) attn_fa_ker
     v_dst[u] = r * 256 + ((p_chunk ^ (4 * (r & 3))) << 4);
   }
   u32x4 kreg[2][NP], vreg[2][NP];   // two staging sets (the second one only when DEEP)
+  int poff[NP];                      // paged: byte offsets of this thread's pieces of one tile
   const int ntile = (kend - kbeg + kFaTile - 1) / kFaTile;
 
+  // Paged piece offsets of tile T (shared by its K and V loads).
+#define FA_POFF(T)                                                                               \
+  if constexpr (PAGED) {                                                                         \
+    _Pragma("unroll") for (int u = 0; u < NP; ++u) {                                             \
+      const int key_ = kbeg + (T) * kFaTile + p_row + 4 * W * u;                                 \
+      const int tok_ = paged_tok(key_);                                                          \
+      poff[u] = key_ < kend && tok_ < si.n_seq ? tok_ * (int)tstride * 2 + p_chunk * 16 : nrec; \
+    }                                                                                            \
+  }
+#define FA_OFF(T, U) (PAGED ? poff[U] : (T) * kFaTile * (int)tstride * 2 + g_off + (U) * g_step)
   // Buffer loads: rows past the chunk end read as zero (and fetch nothing).
 #define FA_LOAD_K(T, SET)                                                                        \
   _Pragma("unroll") for (int u = 0; u < NP; ++u) kreg[SET][u] = __builtin_bit_cast(u32x4,        \
-      __builtin_amdgcn_raw_buffer_load_b128(krs, (T) * kFaTile * (int)tstride * 2 + g_off + u * g_step, 0, 0));
+      __builtin_amdgcn_raw_buffer_load_b128(krs, FA_OFF(T, u), 0, 0));
 #define FA_LOAD_V(T, SET)                                                                        \
   _Pragma("unroll") for (int u = 0; u < NP; ++u) vreg[SET][u] = __builtin_bit_cast(u32x4,        \
-      __builtin_amdgcn_raw_buffer_load_b128(vrs, (T) * kFaTile * (int)tstride * 2 + g_off + u * g_step, 0, 0));
+      __builtin_amdgcn_raw_buffer_load_b128(vrs, FA_OFF(T, u), 0, 0));
 #define FA_STORE_K(BUF, SET) _Pragma("unroll") for (int u = 0; u < NP; ++u) *(u32x4*)(lds[BUF] + k_dst[u]) = kreg[SET][u];
 #define FA_STORE_V(BUF, SET) _Pragma("unroll") for (int u = 0; u < NP; ++u) *(u32x4*)(lds[BUF] + kFaTileBytes + v_dst[u]) = vreg[SET][u];
 
@@ -230,10 +265,23 @@ __global__ void __launch_bounds__(64 * W, QT == 1 && W == 4 ? 2 : 1) attn_fa_ker
     f32x16 acc[QT][2];
 #define FA_DEEP_ITER(T, CUR)                                                                     \
   {                                                                                              \
+    FA_POFF((T) + 2);                                                                            \
     FA_LOAD_K((T) + 2, CUR);                                                                     \
     FA_LOAD_V((T) + 2, CUR);                                                                     \
+    uint64_t vm_ = ~0ull;                                                                        \
+    if constexpr (PAGED) {   /* validity of the tile's keys: lane = key */                       \
+      const int key_ = kbeg + (T) * kFaTile + lane;                                              \
+      vm_ = __ballot(key_ < kend && paged_tok(key_) < si.n_seq);                                 \
+    }                                                                                            \
     FA_QK(acc, lds[CUR]);                                                                        \
-    if ((T) == ntile - 1) {                                                                      \
+    if (PAGED && vm_ != ~0ull) {   /* register r of half s holds key 32 s + 8 (r >> 2) + 4 g + (r & 3) */ \
+      _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                            \
+        const uint32_t wg_ = (uint32_t)(vm_ >> (32 * s)) >> (4 * g);                             \
+        _Pragma("unroll") for (int r = 0; r < 16; ++r)                                           \
+          if (!((wg_ >> (8 * (r >> 2) + (r & 3))) & 1u))                                         \
+            _Pragma("unroll") for (int qi = 0; qi < QT; ++qi) acc[qi][s][r] = kNegInf;           \
+      }                                                                                          \
+    } else if (!PAGED && (T) == ntile - 1) {                                                     \
       const int kvalid = kend - kbeg - (T) * kFaTile;                                            \
       if (kvalid < kFaTile)                                                                      \
         _Pragma("unroll") for (int s = 0; s < 2; ++s)                                            \
@@ -248,8 +296,10 @@ __global__ void __launch_bounds__(64 * W, QT == 1 && W == 4 ? 2 : 1) attn_fa_ker
     FA_STORE_V((CUR) ^ 1, (CUR) ^ 1);                                                            \
     __syncthreads();                                                                             \
   }
+    FA_POFF(0);
     FA_LOAD_K(0, 0);
     FA_LOAD_V(0, 0);
+    FA_POFF(1);
     FA_LOAD_K(1, 1);
     FA_LOAD_V(1, 1);
     FA_STORE_K(0, 0);
@@ -316,6 +366,8 @@ __global__ void __launch_bounds__(64 * W, QT == 1 && W == 4 ? 2 : 1) attn_fa_ker
     FA_PV(pb, lds[(ntile - 1) & 1] + kFaTileBytes);
   }
   }
+#undef FA_POFF
+#undef FA_OFF
 #undef FA_LOAD_K
 #undef FA_LOAD_V
 #undef FA_STORE_K
@@ -350,11 +402,18 @@ __global__ void __launch_bounds__(64 * W, QT == 1 && W == 4 ? 2 : 1) attn_fa_ker
   }
 }
 
-// bf16, d = 128, no paged source, chunks whole 64-key tiles apart; the K offsets of one
-// chunk are 32-bit.
+// bf16, d = 128, chunks whole 64-key tiles apart; the K offsets of one chunk (contiguous)
+// or one sequence (paged) are 32-bit.  A paged source needs a power-of-two page size, at
+// most 128 rows (the deep-prefetch variant) and a chunk page list that fits in LDS.
 bool fa_ok(const AttnArgs& a, const AttnSrc& s) {
   if (s.n_splits == 0) return true;
-  if (a.d != 128 || s.pages) return false;
+  if (a.d != 128) return false;
+  if (s.pages) {
+    const int P = s.page_size;
+    if (P < 1 || (P & (P - 1)) || fa_waves(s.rows) != 4) return false;
+    if (s.chunk / P + 2 > kFaMaxChunkPages) return false;
+    return (int64_t)a.max_seqlen * a.h_kv * 128 * 2 < ((int64_t)1 << 31);
+  }
   return (int64_t)s.chunk * a.h_kv * 128 * 2 < ((int64_t)1 << 31);
 }
 
@@ -367,15 +426,22 @@ hipError_t launch_fa(const AttnArgs& a, hipStream_t st) {
   const int64_t n = items(a.src0) + items(a.src1);
   if (n == 0) return hipSuccess;
   if (n >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  // both sources of a launch are paged (selected / complement pages) or neither is
+  const bool paged = (a.src0.n_splits ? a.src0.pages : a.src1.pages) != nullptr;
+  if (a.src0.n_splits && a.src1.n_splits && (a.src0.pages != nullptr) != (a.src1.pages != nullptr))
+    return hipErrorInvalidValue;
+  if (paged && fa_waves(rows) != 4) return hipErrorInvalidValue;
   // up to 128 rows the pass streams K / V (deep prefetch); larger groups are matrix bound
-  if (fa_waves(rows) == 4)
-    hipLaunchKernelGGL((attn_fa_kernel<kFaQt, 4, true>), dim3((unsigned)n), dim3(256), 0, st, a);
+  if (paged)
+    hipLaunchKernelGGL((attn_fa_kernel<kFaQt, 4, true, true>), dim3((unsigned)n), dim3(256), 0, st, a);
+  else if (fa_waves(rows) == 4)
+    hipLaunchKernelGGL((attn_fa_kernel<kFaQt, 4, true, false>), dim3((unsigned)n), dim3(256), 0, st, a);
   else if (FB_FA_BIG == 1)
-    hipLaunchKernelGGL((attn_fa_kernel<2, 4, true>), dim3((unsigned)n), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_fa_kernel<2, 4, true, false>), dim3((unsigned)n), dim3(256), 0, st, a);
   else if (FB_FA_BIG == 2)
-    hipLaunchKernelGGL((attn_fa_kernel<2, 4, false>), dim3((unsigned)n), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_fa_kernel<2, 4, false, false>), dim3((unsigned)n), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_fa_kernel<kFaQt, 8, false>), dim3((unsigned)n), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((attn_fa_kernel<kFaQt, 8, false, false>), dim3((unsigned)n), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 

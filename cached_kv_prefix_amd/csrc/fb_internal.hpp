@@ -84,6 +84,7 @@ constexpr int kStreamTmax = FB_STREAM_TMAX;
 #endif
 constexpr int kFaQt = FB_FA_QT;
 constexpr int kFaMinRows = 33;
+constexpr int kFaMaxChunkPages = 2048;   // page list of one paged chunk, staged in LDS
 inline int fa_waves(int rows) { return rows <= 128 * kFaQt ? 4 : 8; }
 inline int fa_rows_per_item(int rows) { return 32 * kFaQt * fa_waves(rows); }
 

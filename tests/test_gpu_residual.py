@@ -48,6 +48,9 @@ SMALL = [
     ("mha_stream", 1, 4, 4, 128, 16, [1000], 16, 20, "bf16"),
     ("gqa_ragged_stream", 2, 8, 2, 128, 8, [517, 93], 16, 9, "bf16"),
     ("rows64_tiled", 1, 2, 2, 128, 64, [700], 16, 11, "bf16"),
+    ("rows64_page256", 1, 4, 2, 128, 32, [3000], 256, 5, "bf16"),
+    ("gqa_rows128_page32", 2, 8, 2, 128, 32, [2100, 700], 32, 30, "bf16"),
+    ("rows160_generic", 1, 5, 1, 128, 32, [800], 16, 12, "bf16"),
     ("page8", 1, 4, 2, 128, 16, [333], 8, 13, "bf16"),
     ("page48_long", 1, 2, 2, 128, 16, [9000], 48, 40, "bf16"),
     ("d64", 2, 4, 2, 64, 8, [260, 129], 16, 6, "bf16"),
