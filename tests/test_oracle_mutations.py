@@ -129,3 +129,24 @@ def test_residual_reuse_that_recomputes_is_caught(monkeypatch):
     real = OR.step
     monkeypatch.setattr(TR, "step", lambda *a: real(*a[:8], np.zeros_like(a[8]), *a[9:]))
     assert _fails(TR.test_stale_residual_persists_and_only_reusing_heads_keep_it)
+
+
+def test_lifecycle_mask_from_previous_step_count_is_caught(monkeypatch):
+    """Reading M of the previous step for the threshold decision breaks the fresh/reuse pin."""
+    import oracle.lifecycle as LC
+    import tests.test_oracle_lifecycle as TLC
+    real = LC.block_run
+
+    def shifted(q, k, v, cu, kb, vb, scale, rule, m_steps=None, tau=None, gamma=None):
+        m2 = None if m_steps is None else np.concatenate([m_steps[:1], m_steps[:-1]])
+        return real(q, k, v, cu, kb, vb, scale, rule, m_steps=m2, tau=tau, gamma=gamma)
+    monkeypatch.setattr(LC, "block_run", shifted)
+    assert _fails(TLC.test_threshold_run_fresh_steps_are_full_attention_and_reuse_keeps_step0)
+
+
+def test_lifecycle_append_order_is_caught(monkeypatch):
+    import oracle.lifecycle as LC
+    import tests.test_oracle_lifecycle as TLC
+    real = LC.append_block
+    monkeypatch.setattr(LC, "append_block", lambda k, v, cu, kb, vb: real(k, v, cu, kb[:, ::-1], vb[:, ::-1]))
+    assert _fails(TLC.test_append_tokens_by_brute_force)
