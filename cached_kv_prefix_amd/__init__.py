@@ -18,7 +18,9 @@ STATUS = {0: "FB_OK", 1: "FB_ERR_INVALID_ARG", 2: "FB_ERR_UNSUPPORTED", 3: "FB_E
 EXPORTS = ("fb_status_string", "fb_workspace_size", "fb_prefix_attn", "fb_block_attn", "fb_lse_merge",
            "fb_step", "fb_step_threshold", "fb_mask_threshold", "fb_mask_similarity", "fb_head_cosine", "losa_meta_bytes",
            "losa_workspace_size", "losa_union_capacity", "losa_page_meta", "losa_select_union", "losa_step",
-           "fb_residual_workspace_size", "fb_residual_step")
+           "fb_residual_workspace_size", "fb_residual_step", "fb_append_block", "losa_page_meta_append",
+           "fb_block_workspace_size", "fb_block_run")
+FB_RULE_THRESHOLD, FB_RULE_SIMILARITY = 0, 1
 
 
 class FlashBlockError(RuntimeError):
@@ -43,6 +45,10 @@ class ResidualShape(C.Structure):
     _fields_ = [("s", FbShape), ("page_size", C.c_int32), ("max_pages", C.c_int32), ("max_sel", C.c_int32)]
 
 
+class BlockPlan(C.Structure):
+    _fields_ = [("n_steps", C.c_int32), ("rule", C.c_int32), ("tau", C.c_int32), ("gamma", C.c_float)]
+
+
 class FbTrace(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("attn_begin", "attn_end", "merge_begin", "merge_end",
                                            "select_begin", "select_end")]
@@ -63,6 +69,7 @@ def load(path: str | None = None):
     vp, i32, i64, f32, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
     sp, lp, tp = C.POINTER(FbShape), C.POINTER(LosaShape), C.POINTER(FbTrace)
     rp = C.POINTER(ResidualShape)
+    bp = C.POINTER(BlockPlan)
     sig = {
         "fb_status_string": (C.c_char_p, [i32]),
         "fb_workspace_size": (sz, [sp]),
@@ -82,6 +89,10 @@ def load(path: str | None = None):
         "losa_step": (i32, [lp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, tp, vp]),
         "fb_residual_workspace_size": (sz, [rp]),
         "fb_residual_step": (i32, [rp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, tp, vp]),
+        "fb_append_block": (i32, [sp, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "losa_page_meta_append": (i32, [lp, i32, vp, vp, vp, vp]),
+        "fb_block_workspace_size": (sz, [sp]),
+        "fb_block_run": (i32, [sp, bp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -247,3 +258,25 @@ def residual_step(rs, q, k, v, k_blk, v_blk, sel_pages, sel_count, reuse_mask, c
                                    0 if ws is None else ws.numel() * ws.element_size(),
                                    None if trace is None else C.byref(trace), _stream(stream)),
            "fb_residual_step")
+
+
+def append_block(shape, k, v, k_blk, v_blk, k_out, v_out, cu_out=None, stream=None):
+    _check(load().fb_append_block(C.byref(shape), _ptr(k), _ptr(v), _ptr(k_blk), _ptr(v_blk), _ptr(k_out),
+                                  _ptr(v_out), _ptr(cu_out), _stream(stream)), "fb_append_block")
+
+
+def losa_page_meta_append(ls, n_appended, k, kmin, kmax, stream=None):
+    _check(load().losa_page_meta_append(C.byref(ls), n_appended, _ptr(k), _ptr(kmin), _ptr(kmax), _stream(stream)),
+           "losa_page_meta_append")
+
+
+def block_workspace_size(shape) -> int:
+    return int(load().fb_block_workspace_size(C.byref(shape)))
+
+
+def block_run(shape, plan, q_steps, k, v, k_blk_steps, v_blk_steps, m_steps, cache_a, cache_l, a_full_steps,
+              l_full_steps, masks, sims, ws, stream=None):
+    _check(load().fb_block_run(C.byref(shape), C.byref(plan), _ptr(q_steps), _ptr(k), _ptr(v), _ptr(k_blk_steps),
+                               _ptr(v_blk_steps), _ptr(m_steps), _ptr(cache_a), _ptr(cache_l), _ptr(a_full_steps),
+                               _ptr(l_full_steps), _ptr(masks), _ptr(sims), _ptr(ws),
+                               0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)), "fb_block_run")

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 OBJ = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(HERE, "libflashblock.so")
-SOURCES = ["fb_attn.hip", "fb_stream.hip", "fb_fa.hip", "fb_combine.hip", "fb_losa.hip", "fb_residual.hip", "fb_api.hip"]
+SOURCES = ["fb_attn.hip", "fb_stream.hip", "fb_fa.hip", "fb_combine.hip", "fb_losa.hip", "fb_residual.hip", "fb_lifecycle.hip", "fb_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

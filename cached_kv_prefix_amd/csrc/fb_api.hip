@@ -466,7 +466,7 @@ fb_status losa_page_meta(const losa_shape* ls, const void* k, void* kmin, void* 
   if (st != FB_OK) return st;
   if (!kmin || !kmax || !aligned16(kmin) || !aligned16(kmax)) return FB_ERR_INVALID_ARG;
   if (!k && !prefix_may_be_empty(&ls->s)) return FB_ERR_INVALID_ARG;
-  return hip_status(launch_page_meta(losa_args(ls), k, kmin, kmax, stream));
+  return hip_status(launch_page_meta(losa_args(ls), k, kmin, kmax, 0, stream));
 }
 
 fb_status losa_select_union(const losa_shape* ls, const void* q_cur, const void* q_prev, const void* kmin,
@@ -691,6 +691,137 @@ fb_status fb_residual_step(const fb_residual_shape* rs, const void* q, const voi
   rec(trace ? trace->merge_begin : nullptr, stream);
   if (hipError_t e = launch_combine(c, stream)) return hip_status(e);
   rec(trace ? trace->merge_end : nullptr, stream);
+  return FB_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------
+// Block lifecycle: append, page metadata of the new pages, and the steps of one block
+// ---------------------------------------------------------------------------------------
+namespace {
+
+inline size_t el_size(const fb_shape* s) { return s->dtype == FB_BF16 ? 2 : 4; }
+
+struct BlockPlan {
+  StepPlan step;
+  size_t prev_off, sim_off, ws_bytes;
+};
+BlockPlan block_plan(const fb_shape* s) {
+  BlockPlan p;
+  p.step = step_plan(s);
+  p.prev_off = align256(p.step.ws_bytes);
+  p.sim_off = align256(p.prev_off + (size_t)s->batch * s->block * s->h_q * s->head_dim * sizeof(float));
+  p.ws_bytes = align256(p.sim_off + (size_t)s->batch * s->h_q * sizeof(float));
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+fb_status fb_append_block(const fb_shape* s, const void* k, const void* v, const void* k_blk, const void* v_blk,
+                          void* k_out, void* v_out, int32_t* cu_out, hipStream_t stream) {
+  fb_status st = check_shape(s);
+  if (st != FB_OK) return st;
+  if (!k_blk || !v_blk || !k_out || !v_out) return FB_ERR_INVALID_ARG;
+  if (!prefix_may_be_empty(s) && (!k || !v)) return FB_ERR_INVALID_ARG;
+  const size_t row_bytes = (size_t)s->h_kv * s->head_dim * el_size(s);
+  const uintptr_t need = row_bytes % 16 == 0 ? 15u : 3u;
+  for (const void* p : {k, v, k_blk, v_blk, (const void*)k_out, (const void*)v_out})
+    if (p && ((uintptr_t)p & need)) return FB_ERR_INVALID_ARG;
+  const bool in_place = k_out == k && v_out == v && k != nullptr;
+  if ((k_out == k) != (v_out == v) && k != nullptr) return FB_ERR_INVALID_ARG;
+  if (in_place && s->batch != 1) return FB_ERR_INVALID_ARG;   // later sequences would move
+  if (cu_out && (const int32_t*)cu_out == s->cu_seqlens_k) return FB_ERR_INVALID_ARG;
+  if ((int64_t)s->batch * (max_prefix(s) + (int64_t)s->block) >= INT32_MAX) return FB_ERR_UNSUPPORTED;
+  AppendArgs a;
+  a.k = k;
+  a.v = v;
+  a.cu = s->cu_seqlens_k;
+  a.n_uniform = s->seqlen_k;
+  a.k_blk = k_blk;
+  a.v_blk = v_blk;
+  a.k_out = k_out;
+  a.v_out = v_out;
+  a.cu_out = cu_out;
+  a.batch = s->batch;
+  a.B = s->block;
+  a.max_len = max_prefix(s);
+  a.row_bytes = (int64_t)row_bytes;
+  a.tail_only = in_place ? 1 : 0;
+  return hip_status(launch_append(a, stream));
+}
+
+fb_status losa_page_meta_append(const losa_shape* ls, int32_t n_appended, const void* k, void* kmin, void* kmax,
+                                hipStream_t stream) {
+  fb_status st = check_losa(ls);
+  if (st != FB_OK) return st;
+  if (n_appended < 1) return FB_ERR_INVALID_ARG;
+  if (!k || !kmin || !kmax || !aligned16(kmin) || !aligned16(kmax)) return FB_ERR_INVALID_ARG;
+  return hip_status(launch_page_meta(losa_args(ls), k, kmin, kmax, n_appended, stream));
+}
+
+size_t fb_block_workspace_size(const fb_shape* s) {
+  if (check_shape(s) != FB_OK) return 0;
+  return block_plan(s).ws_bytes;
+}
+
+fb_status fb_block_run(const fb_shape* s, const fb_block_plan* plan, const void* q_steps, const void* k,
+                       const void* v, const void* k_blk_steps, const void* v_blk_steps, const int32_t* m_steps,
+                       float* cache_a, float* cache_l, void* a_full_steps, float* l_full_steps, uint8_t* masks,
+                       float* sims, void* ws, size_t ws_bytes, hipStream_t stream) {
+  fb_status st = check_shape(s);
+  if (st != FB_OK) return st;
+  if (!plan || plan->n_steps < 1) return FB_ERR_INVALID_ARG;
+  if (plan->rule != FB_RULE_THRESHOLD && plan->rule != FB_RULE_SIMILARITY) return FB_ERR_INVALID_ARG;
+  if (plan->rule == FB_RULE_THRESHOLD && !m_steps) return FB_ERR_INVALID_ARG;
+  if (plan->rule == FB_RULE_SIMILARITY && !(plan->gamma == plan->gamma)) return FB_ERR_INVALID_ARG;
+  if ((st = check_inputs(s, q_steps, k, v)) != FB_OK) return st;
+  if (!k_blk_steps || !v_blk_steps || !aligned16(k_blk_steps) || !aligned16(v_blk_steps)) return FB_ERR_INVALID_ARG;
+  if (!cache_a || !cache_l || !a_full_steps || !masks || !aligned16(cache_a)) return FB_ERR_INVALID_ARG;
+  const BlockPlan p = block_plan(s);
+  if (ws_bytes < p.ws_bytes || !ws || !aligned16(ws)) return FB_ERR_WORKSPACE;
+  const int64_t bh = (int64_t)s->batch * s->h_q;
+  const int64_t q_elems = bh * s->block * s->head_dim;
+  const int64_t kb_elems = (int64_t)s->batch * s->block * s->h_kv * s->head_dim;
+  const size_t el = el_size(s);
+  // every step's operands stay 16-byte aligned
+  if ((q_elems * el) % 16 != 0 || (kb_elems * el) % 16 != 0) return FB_ERR_UNSUPPORTED;
+  float* prev = (float*)((char*)ws + p.prev_off);
+  float* sim_ws = (float*)((char*)ws + p.sim_off);
+  const bool cos_needed = plan->rule == FB_RULE_SIMILARITY || sims != nullptr;
+  const float* sim_prev = nullptr;
+  for (int step = 0; step < plan->n_steps; ++step) {
+    uint8_t* m = masks + step * bh;
+    hipError_t e;
+    if (plan->rule == FB_RULE_THRESHOLD)
+      e = step == 0 ? launch_fill_u8(m, bh, 0, stream)
+                    : launch_mask_threshold(m_steps + (int64_t)step * s->batch, plan->tau, s->batch, s->h_q, m, stream);
+    else
+      e = step < 2 ? launch_fill_u8(m, bh, 0, stream) : launch_mask_similarity(sim_prev, plan->gamma, bh, m, stream);
+    if (e != hipSuccess) return hip_status(e);
+    if (cos_needed && step >= 1)
+      if ((e = launch_copy_f32(cache_a, prev, q_elems, stream)) != hipSuccess) return hip_status(e);
+    const char* qs = (const char*)q_steps + step * q_elems * el;
+    const char* kbs = (const char*)k_blk_steps + step * kb_elems * el;
+    const char* vbs = (const char*)v_blk_steps + step * kb_elems * el;
+    char* af = (char*)a_full_steps + step * q_elems * el;
+    float* lf = l_full_steps ? l_full_steps + step * bh * s->block : nullptr;
+    st = run_step(s, qs, k, v, kbs, vbs, m, nullptr, 0, cache_a, cache_l, af, lf, ws, p.step.ws_bytes, nullptr,
+                  stream);
+    if (st != FB_OK) return st;
+    float* sim_s = sims ? sims + step * bh : sim_ws;
+    if (cos_needed) {
+      if (step == 0) {
+        if (sims && (e = launch_fill_f32(sim_s, bh, __builtin_nanf(""), stream)) != hipSuccess) return hip_status(e);
+      } else if ((e = launch_head_cosine(s->batch, s->block, s->h_q, s->head_dim, prev, cache_a, sim_s, stream)) !=
+                 hipSuccess) {
+        return hip_status(e);
+      }
+    }
+    sim_prev = sim_s;
+  }
   return FB_OK;
 }
 

@@ -112,7 +112,7 @@ struct LosaArgs {
   int32_t page_size, topk, n_active, max_pages, max_union;
   int32_t bf16;
 };
-hipError_t launch_page_meta(const LosaArgs& a, const void* k, void* kmin, void* kmax,
+hipError_t launch_page_meta(const LosaArgs& a, const void* k, void* kmin, void* kmax, int tail,
                             hipStream_t st);
 hipError_t launch_locality(const LosaArgs& a, const void* qc, const void* qp, double* loc,
                            int32_t* active, hipStream_t st);
@@ -137,5 +137,21 @@ struct ResidualArgs {
 };
 constexpr int kResidualMaxPages = 65536;
 hipError_t launch_complement(const ResidualArgs& r, hipStream_t st);
+
+// Block lifecycle: append a block to the packed prefix; small fills and copies.
+struct AppendArgs {
+  const void* k; const void* v;           // old prefix, [sum N][h_kv][d]
+  const int32_t* cu; int32_t n_uniform;   // old offsets (or uniform length)
+  const void* k_blk; const void* v_blk;   // [batch][B][h_kv][d]
+  void* k_out; void* v_out;               // new prefix
+  int32_t* cu_out;                        // new offsets or null
+  int32_t batch, B, max_len;              // max_len: bound of every N_b
+  int64_t row_bytes;                      // h_kv * d * element size
+  int32_t tail_only;                      // in place (batch 1): write the block rows only
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t st);
+hipError_t launch_fill_u8(uint8_t* p, int64_t n, uint8_t value, hipStream_t st);
+hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t st);
+hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t st);
 
 }  // namespace fb

@@ -45,16 +45,20 @@ __device__ __forceinline__ uint64_t order_key(double s) {
 
 // kmin/kmax layout [batch][h_kv][d/8][max_pages][8]: consecutive pages of one 8-dim chunk
 // are adjacent, so the score kernel reads them with unit-stride 16-byte (bf16) loads.
-__global__ void __launch_bounds__(256) page_meta_kernel(const LosaArgs a, const void* k, void* kmin, void* kmax) {
+// tail > 0: only the pages that hold one of the last `tail` tokens of each sequence (the
+// grid covers `span` pages from the first of them); tail == 0: every page (span = max_pages).
+__global__ void __launch_bounds__(256) page_meta_kernel(const LosaArgs a, const void* k, void* kmin, void* kmax,
+                                                        int tail, int span) {
   const int b = blockIdx.z, hk = blockIdx.y;
   const int nc = a.d / 8;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)nc * a.max_pages) return;
-  const int c = idx / a.max_pages, p = idx % a.max_pages;
+  if (idx >= (int64_t)nc * span) return;
   int seq0, n;
   seq_of(a, b, seq0, n);
+  const int c = idx / span;
+  const int p = (tail > 0 ? max(0, n - tail) / a.page_size : 0) + (int)(idx % span);
   const int t0 = p * a.page_size;
-  if (t0 >= n) return;
+  if (p >= a.max_pages || t0 >= n) return;
   const int t1 = min(n, t0 + a.page_size);
   float mn[8], mx[8];
   for (int e = 0; e < 8; ++e) {
@@ -433,10 +437,12 @@ __global__ void __launch_bounds__(256) union_kernel(const LosaArgs a, const int3
   if (threadIdx.x == 0) union_count[b * a.h_kv + hk] = total;
 }
 
-hipError_t launch_page_meta(const LosaArgs& a, const void* k, void* kmin, void* kmax, hipStream_t st) {
-  const int64_t n = (int64_t)(a.d / 8) * a.max_pages;
+hipError_t launch_page_meta(const LosaArgs& a, const void* k, void* kmin, void* kmax, int tail, hipStream_t st) {
+  // pages holding the last `tail` tokens: at most ceil(tail / P) + 1 of them
+  const int span = tail > 0 ? min(a.max_pages, (tail + a.page_size - 1) / a.page_size + 1) : a.max_pages;
+  const int64_t n = (int64_t)(a.d / 8) * span;
   dim3 grid((unsigned)((n + 255) / 256), a.h_kv, a.batch);
-  hipLaunchKernelGGL(page_meta_kernel, grid, dim3(256), 0, st, a, k, kmin, kmax);
+  hipLaunchKernelGGL(page_meta_kernel, grid, dim3(256), 0, st, a, k, kmin, kmax, tail, span);
   return hipGetLastError();
 }
 

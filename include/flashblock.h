@@ -263,6 +263,66 @@ fb_status fb_residual_step(const fb_residual_shape* rs, const void* q, const voi
                            float* cache_l, void* a_full, float* l_full, void* ws, size_t ws_bytes,
                            const fb_trace* trace, hipStream_t stream);
 
+/* ------------------------------------------------------------------------------------
+ * Block lifecycle [FB-abs: block-wise causal inference over a KV cache that grows block by
+ * block; FB-pt §2 "Estratégias de Reutilização Adaptativa" for the two reuse rules].
+ * ------------------------------------------------------------------------------------ */
+
+/* Append a finished block to the prefix: for every sequence b the new prefix is the old
+ * one (N_b tokens of k, v as s describes them) followed by the block's B tokens
+ * k_blk[b], v_blk[b].
+ *   k_out, v_out [sum_b (N_b + B)][h_kv][d] (dtype); cu_out: device int32 [batch + 1]
+ *   receives the new offsets (cu[b] + b*B, or b*(seqlen_k + B) for a uniform prefix); it
+ *   may be NULL and must not be s->cu_seqlens_k.
+ *   In place (k_out == k and v_out == v) is allowed for batch == 1 only: then only the B
+ *   block rows are written, after the prefix (the buffers must hold N + B tokens).  Any
+ *   other overlap of outputs and inputs is not allowed.  k, v may be NULL for an empty
+ *   uniform prefix. */
+fb_status fb_append_block(const fb_shape* s, const void* k, const void* v, const void* k_blk,
+                          const void* v_blk, void* k_out, void* v_out, int32_t* cu_out,
+                          hipStream_t stream);
+
+/* Page metadata after an append: ls describes the grown prefix; the pages that hold one of
+ * the last n_appended tokens of each sequence are rebuilt from k, the others are left as
+ * they are.  When kmin/kmax held the metadata of the old prefix the result equals
+ * losa_page_meta over the grown prefix, bit for bit. */
+fb_status losa_page_meta_append(const losa_shape* ls, int32_t n_appended, const void* k,
+                                void* kmin, void* kmax, hipStream_t stream);
+
+typedef enum fb_reuse_rule { FB_RULE_THRESHOLD = 0, FB_RULE_SIMILARITY = 1 } fb_reuse_rule;
+
+typedef struct fb_block_plan {
+  int32_t n_steps;   /* S >= 1 denoising steps of the block                                 */
+  int32_t rule;      /* fb_reuse_rule                                                        */
+  int32_t tau;       /* threshold rule: sequence b reuses at step s >= 1 when M_s[b] < tau   */
+  float gamma;       /* similarity rule: head h reuses at step s >= 2 when sim_{s-1} > gamma  */
+} fb_block_plan;
+
+/* Workspace bytes for fb_block_run (a step's workspace, a copy of cache_a, similarities). */
+size_t fb_block_workspace_size(const fb_shape* s);
+
+/* The S steps of one block, each an fb_step, with the reuse mask of every step chosen by
+ * the plan's rule and recorded in masks (the reuse statistics):
+ *   threshold: step 0 refreshes every head; step s >= 1 uses fb_mask_threshold(M_s, tau);
+ *   similarity: after step s >= 1, sim_s[b][h] = fb_head_cosine(cache_a before step s,
+ *     cache_a after it) (two consecutive computed A_out of the head; a head that reused
+ *     keeps its cache, so its similarity is 1); steps 0 and 1 refresh every head, step
+ *     s >= 2 uses fb_mask_similarity(sim_{s-1}, gamma).
+ * Per-step operands are consecutive in memory:
+ *   q_steps [S][batch][B][h_q][d]; k_blk_steps, v_blk_steps [S][batch][B][h_kv][d];
+ *   m_steps [S][batch] int32 (threshold rule; step 0's entry is not read);
+ *   a_full_steps [S][batch][B][h_q][d] (dtype); l_full_steps [S][batch][B][h_q] or NULL;
+ *   masks [S][batch][h_q] uint8 (output); sims [S][batch][h_q] fp32 or NULL (output; step
+ *   0 holds NaN; with the threshold rule the similarities are reported, not used).
+ * cache_a / cache_l: the cache, left holding the last step's values; its contents on entry
+ * are not read (step 0 refreshes).  One step's q and block K/V must be a multiple of 16 bytes
+ * (FB_ERR_UNSUPPORTED otherwise). */
+fb_status fb_block_run(const fb_shape* s, const fb_block_plan* plan, const void* q_steps,
+                       const void* k, const void* v, const void* k_blk_steps,
+                       const void* v_blk_steps, const int32_t* m_steps, float* cache_a,
+                       float* cache_l, void* a_full_steps, float* l_full_steps, uint8_t* masks,
+                       float* sims, void* ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

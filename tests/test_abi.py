@@ -180,3 +180,30 @@ def test_residual_step_rejects_bad_args_before_launch():
     assert call(nb=n - 1) == 3 and call(ws=None) == 3
     bad = residual_shape(max_sel=0)
     assert lib.fb_residual_step(C.byref(bad), f, f, f, f, f, f, f, None, f, f, f, None, f, n, None, None) == 1
+
+
+def test_lifecycle_validation():
+    lib = fb.load()
+    f = C.c_void_p(0x10000)
+    s = dllm_shape(batch=2)
+    # in place with more than one sequence would move the later sequences
+    assert lib.fb_append_block(C.byref(s), f, f, f, f, f, f, None, None) == 1
+    g = C.c_void_p(0x20000)
+    assert lib.fb_append_block(C.byref(s), f, f, f, f, g, f, None, None) == 1      # only k in place
+    assert lib.fb_append_block(C.byref(s), f, f, None, f, g, g, None, None) == 1
+    plan = fb.BlockPlan(0, fb.FB_RULE_THRESHOLD, 4, 0.0)
+    n = fb.block_workspace_size(s)
+    assert n > fb.workspace_size(s)
+    args = [f, f, f, f, f, f, f, f, f, None, f, None, f, n, None]
+    assert lib.fb_block_run(C.byref(s), C.byref(plan), *args) == 1                  # no steps
+    plan = fb.BlockPlan(4, 7, 4, 0.0)
+    assert lib.fb_block_run(C.byref(s), C.byref(plan), *args) == 1                  # unknown rule
+    plan = fb.BlockPlan(4, fb.FB_RULE_THRESHOLD, 4, 0.0)
+    a2 = list(args)
+    a2[5] = None
+    assert lib.fb_block_run(C.byref(s), C.byref(plan), *a2) == 1                    # threshold without M
+    a3 = list(args)
+    a3[13] = n - 1
+    assert lib.fb_block_run(C.byref(s), C.byref(plan), *a3) == 3
+    ls = losa_shape()
+    assert lib.losa_page_meta_append(C.byref(ls), 0, f, f, f, None) == 1
