@@ -104,6 +104,20 @@ def run_step(fb, shape, dev, bufs, mask_src=None, tau=4, trace=None, sim=None, g
             bufs["af"], bufs["lf"], bufs["ws"], trace=trace)
 
 
+def wall_time(fn, steps, warmup):
+    """Warm up, then the wall time per call of `steps` calls back to back (synchronised on
+    both sides)."""
+    import torch
+    for _ in range(warmup):
+        fn(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn(None)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
 def time_steps(fn, steps, warmup):
     """Warm up, then time `steps` calls back to back (synchronised on both sides): the wall
     time per step.  A second pass of `steps` calls has the library record a HIP event pair
@@ -300,6 +314,7 @@ def main():
         extra["cold_fresh_step_us"] = flushed_step_times(lambda tr: run_step(fb, shape, dev, bufs, m_fresh)) * 1e6
         extra["workloads"] = other_workloads(fb, args)
         extra["context_sweep"] = context_sweep(fb, args)
+        extra["lifecycle"] = lifecycle_workload(fb, args)
     result = {
         "metric": "attn step µs & KV GB/s (B=32, 32k prefix, bf16); % of HBM/MFMA peak",
         "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -358,6 +373,62 @@ def context_sweep(fb, args, lengths=(102400, 204800, 409600, 819200)):
     return {"points": out, "fresh_growth_us": f1 - f0, "block8_growth_us": b1 - b0,
             "growth_ratio_block8_over_fresh": (b1 - b0) / (f1 - f0),
             "fresh_steps_per_block": int(1 + (synth.dllm().extra["m_updated"][1:, 0] >= 4).sum())}
+
+
+def lifecycle_workload(fb, args, blocks=4, S=8):
+    """Multi-block run on the dLLM step shape (32 heads, d 128, B 32): a prefix of 32768
+    tokens grows by one block per block.  Per block: fb_block_run over S steps under the
+    threshold rule (tau 4; M drawn as in the dLLM workload, one draw per block), then
+    fb_append_block in place.  Per-step queries drift by N(0, 0.01^2) around the block's
+    queries and the block K/V by N(0, 0.05^2); inputs are drawn on the device from a seeded
+    generator.  Reports the time per block and per step, and the reuse statistics (the
+    masks each step used, and the per-head cosine of consecutive prefix outputs)."""
+    import torch
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(13)
+    H, d, B, N0 = 32, 128, 32, 32768
+    g = np.random.Generator(np.random.PCG64(13))
+    m_all = g.integers(0, 9, size=(blocks, S, 1)).astype(np.int32)
+
+    def draw(*shape, std=1.0 / np.sqrt(128.0)):
+        return (torch.randn(*shape, generator=gen, device="cuda") * std).to(torch.bfloat16)
+    cap = N0 + blocks * B
+    k = torch.empty((cap, H, d), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty_like(k)
+    k[:N0] = draw(N0, H, d)
+    v[:N0] = draw(N0, H, d)
+    plan = fb.BlockPlan(S, fb.FB_RULE_THRESHOLD, 4, 0.0)
+    per_block = []
+    for j in range(blocks):
+        q0, kb0, vb0 = draw(1, B, H, d), draw(1, B, H, d), draw(1, B, H, d)
+        q = torch.stack([q0 + draw(1, B, H, d, std=0.01) for _ in range(S)])
+        kb = torch.stack([kb0 + draw(1, B, H, d, std=0.05) for _ in range(S)])
+        vb = torch.stack([vb0 + draw(1, B, H, d, std=0.05) for _ in range(S)])
+        n = N0 + j * B
+        shape = fb.make_shape(1, H, H, d, B, seqlen_k=n)
+        bufs = dict(ca=torch.zeros((1, B, H, d), device="cuda"), cl=torch.zeros((1, B, H), device="cuda"),
+                    af=torch.empty((S, 1, B, H, d), dtype=torch.bfloat16, device="cuda"),
+                    masks=torch.empty((S, 1, H), dtype=torch.uint8, device="cuda"),
+                    sims=torch.empty((S, 1, H), device="cuda"),
+                    ws=torch.empty(fb.block_workspace_size(shape), dtype=torch.uint8, device="cuda"))
+        m = torch.from_numpy(m_all[j]).cuda()
+
+        def run(tr):
+            fb.block_run(shape, plan, q, k, v, kb, vb, m, bufs["ca"], bufs["cl"], bufs["af"], None, bufs["masks"],
+                         bufs["sims"], bufs["ws"])
+        wall = wall_time(run, max(3, args.steps // 10), 1)
+        fb.append_block(shape, k, v, kb[-1], vb[-1], k, v)   # in place: the block follows the prefix
+        masks = bufs["masks"].cpu().numpy()
+        sims = bufs["sims"].cpu().numpy()[1:]
+        per_block.append({"prefix": n, "block_us": wall * 1e6, "step_mean_us": wall / S * 1e6,
+                          "reused_head_steps": int(masks.sum()), "head_steps": int(masks.size),
+                          "sim_min": float(np.nanmin(sims)), "sim_mean": float(np.nanmean(sims))})
+    torch.cuda.synchronize()
+    reused = sum(b_["reused_head_steps"] for b_ in per_block)
+    total = sum(b_["head_steps"] for b_ in per_block)
+    return {"blocks": per_block, "reuse_fraction": reused / total,
+            "step_mean_us": float(np.mean([b_["step_mean_us"] for b_ in per_block])),
+            "prefix_final": N0 + blocks * B}
 
 
 def other_workloads(fb, args):
