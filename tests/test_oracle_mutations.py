@@ -150,3 +150,18 @@ def test_lifecycle_append_order_is_caught(monkeypatch):
     real = LC.append_block
     monkeypatch.setattr(LC, "append_block", lambda k, v, cu, kb, vb: real(k, v, cu, kb[:, ::-1], vb[:, ::-1]))
     assert _fails(TLC.test_append_tokens_by_brute_force)
+
+
+def test_varlen_branch_prefix_off_by_one_is_caught(monkeypatch):
+    """Reading the next branch's first prefix token (cu_k[b+1] + 1 as the end) breaks the
+    brute-force pin."""
+    import oracle.varlen as OV
+    import tests.test_oracle_varlen as TV
+    real = OV.prefix_attention_varlen
+
+    def shifted(q, cu_q, k, v, cu_k, h_kv, scale):
+        ck = np.asarray(cu_k).copy()
+        ck[1:-1] += 1
+        return real(q, cu_q, k, v, ck, h_kv, scale)
+    monkeypatch.setattr(TV, "prefix_attention_varlen", shifted)
+    assert _fails(TV.test_branches_are_independent_and_brute_force)
