@@ -19,7 +19,8 @@ EXPORTS = ("fb_status_string", "fb_workspace_size", "fb_prefix_attn", "fb_block_
            "fb_step", "fb_step_threshold", "fb_mask_threshold", "fb_mask_similarity", "fb_head_cosine", "losa_meta_bytes",
            "losa_workspace_size", "losa_union_capacity", "losa_page_meta", "losa_select_union", "losa_step",
            "fb_residual_workspace_size", "fb_residual_step", "fb_append_block", "losa_page_meta_append",
-           "fb_block_workspace_size", "fb_block_run")
+           "fb_block_workspace_size", "fb_block_run", "fb_prefix_attn_varlen_workspace_size",
+           "fb_prefix_attn_varlen")
 FB_RULE_THRESHOLD, FB_RULE_SIMILARITY = 0, 1
 
 
@@ -43,6 +44,10 @@ class LosaShape(C.Structure):
 
 class ResidualShape(C.Structure):
     _fields_ = [("s", FbShape), ("page_size", C.c_int32), ("max_pages", C.c_int32), ("max_sel", C.c_int32)]
+
+
+class VarlenShape(C.Structure):
+    _fields_ = [("s", FbShape), ("cu_seqlens_q", C.c_void_p), ("total_q", C.c_int32)]
 
 
 class BlockPlan(C.Structure):
@@ -70,6 +75,7 @@ def load(path: str | None = None):
     sp, lp, tp = C.POINTER(FbShape), C.POINTER(LosaShape), C.POINTER(FbTrace)
     rp = C.POINTER(ResidualShape)
     bp = C.POINTER(BlockPlan)
+    vlp = C.POINTER(VarlenShape)
     sig = {
         "fb_status_string": (C.c_char_p, [i32]),
         "fb_workspace_size": (sz, [sp]),
@@ -92,6 +98,8 @@ def load(path: str | None = None):
         "fb_append_block": (i32, [sp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "losa_page_meta_append": (i32, [lp, i32, vp, vp, vp, vp]),
         "fb_block_workspace_size": (sz, [sp]),
+        "fb_prefix_attn_varlen_workspace_size": (sz, [vlp]),
+        "fb_prefix_attn_varlen": (i32, [vlp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "fb_block_run": (i32, [sp, bp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
@@ -280,3 +288,17 @@ def block_run(shape, plan, q_steps, k, v, k_blk_steps, v_blk_steps, m_steps, cac
                                _ptr(v_blk_steps), _ptr(m_steps), _ptr(cache_a), _ptr(cache_l), _ptr(a_full_steps),
                                _ptr(l_full_steps), _ptr(masks), _ptr(sims), _ptr(ws),
                                0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)), "fb_block_run")
+
+
+def make_varlen_shape(shape: FbShape, cu_seqlens_q, total_q: int) -> VarlenShape:
+    return VarlenShape(shape, C.c_void_p(cu_seqlens_q.data_ptr()), total_q)
+
+
+def prefix_attn_varlen_workspace_size(vs) -> int:
+    return int(load().fb_prefix_attn_varlen_workspace_size(C.byref(vs)))
+
+
+def prefix_attn_varlen(vs, q, k, v, a_out, l_out, ws, stream=None):
+    _check(load().fb_prefix_attn_varlen(C.byref(vs), _ptr(q), _ptr(k), _ptr(v), _ptr(a_out), _ptr(l_out), _ptr(ws),
+                                        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+           "fb_prefix_attn_varlen")

@@ -826,3 +826,67 @@ fb_status fb_block_run(const fb_shape* s, const fb_block_plan* plan, const void*
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------------------
+// Multi-branch prefix pass over packed variable-length queries
+// ---------------------------------------------------------------------------------------
+namespace {
+
+fb_status check_varlen(const fb_varlen_shape* vs) {
+  if (!vs) return FB_ERR_INVALID_ARG;
+  fb_status st = check_shape(&vs->s);
+  if (st != FB_OK) return st;
+  if (!vs->cu_seqlens_q || vs->total_q < 0) return FB_ERR_INVALID_ARG;
+  if ((int64_t)vs->total_q > (int64_t)vs->s.batch * vs->s.block) return FB_ERR_INVALID_ARG;
+  if ((int64_t)vs->total_q * vs->s.h_q >= INT32_MAX) return FB_ERR_UNSUPPORTED;
+  return FB_OK;
+}
+
+struct VarlenPlan {
+  StepPlan step;
+  size_t rows_off, ws_bytes;
+};
+VarlenPlan varlen_plan(const fb_varlen_shape* vs) {
+  VarlenPlan p;
+  p.step = step_plan(&vs->s);
+  p.rows_off = align256(p.step.ws_bytes);
+  p.ws_bytes = align256(p.rows_off + (size_t)vs->s.batch * vs->s.block * sizeof(int32_t));
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fb_prefix_attn_varlen_workspace_size(const fb_varlen_shape* vs) {
+  if (check_varlen(vs) != FB_OK) return 0;
+  return varlen_plan(vs).ws_bytes;
+}
+
+fb_status fb_prefix_attn_varlen(const fb_varlen_shape* vs, const void* q, const void* k, const void* v,
+                                float* a_out, float* l_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  fb_status st = check_varlen(vs);
+  if (st != FB_OK) return st;
+  const fb_shape* s = &vs->s;
+  if (vs->total_q == 0) return FB_OK;
+  if ((st = check_inputs(s, q, k, v)) != FB_OK) return st;
+  if (!a_out || !l_out) return FB_ERR_INVALID_ARG;
+  const VarlenPlan p = varlen_plan(vs);
+  if (ws_bytes < p.ws_bytes || !ws || !aligned16(ws)) return FB_ERR_WORKSPACE;
+  int32_t* row_tok = (int32_t*)((char*)ws + p.rows_off);
+  if (hipError_t e = launch_varlen_rows(vs->cu_seqlens_q, s->batch, s->block, vs->total_q, row_tok, stream))
+    return hip_status(e);
+  AttnArgs a = base_args(s, q);
+  a.B = 0;   // queries are addressed by the packed row map alone
+  a.src0 = make_src(p.step.rp, p.step.pre, k, v, s->cu_seqlens_k, s->seqlen_k, (float*)ws, p.step.rpre);
+  a.src0.row_tok = row_tok;
+  if (hipError_t e = launch_attn(a, s->dtype == FB_BF16, stream)) return hip_status(e);
+  CombineArgs c = base_combine(s, p.step, (float*)ws);
+  c.mode = kModePrefixOnly;
+  c.cache_a = a_out;
+  c.cache_l = l_out;
+  c.cu_q = vs->cu_seqlens_q;
+  return hip_status(launch_combine(c, stream));
+}
+
+}  // extern "C"

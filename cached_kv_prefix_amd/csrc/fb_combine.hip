@@ -12,7 +12,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs C) {
   if (rowid >= C.batch * C.B * C.h_q) return;
   RowState<E, UP, UB> st;
   row_issue<E, UP, UB>(C, rowid, lane, st);
-  row_finish<E, UP, UB>(C, lane, st);
+  if (st.valid) row_finish<E, UP, UB>(C, lane, st);
 }
 
 template <int E, int UP, int UR, int UB>

@@ -149,7 +149,7 @@ struct RowState {
   float cached[E], cached_l;
   int64_t roff, pslot0, bslot0;
   int rowid, b, i, h, hk, jg, prow, nk;
-  bool fresh;
+  bool fresh, valid;
 };
 
 // UP / UB: prefix / block chunks whose loads are issued up front (further chunks, if
@@ -168,6 +168,13 @@ __device__ __forceinline__ void row_issue(const CombineArgs& C, int rowid, int l
   st.hk = hk;
   st.jg = jg;
   st.roff = (int64_t)rowid * d;
+  st.valid = true;
+  if (C.cu_q) {   // packed variable-length queries: the output row is the packed one
+    const int q0 = C.cu_q[b];
+    st.valid = i < C.cu_q[b + 1] - q0;
+    st.rowid = (q0 + i) * C.h_q + h;
+    st.roff = (int64_t)st.rowid * d;
+  }
   const bool has_prefix = C.mode != kModeBlockOnly;
 
   // the LoSA active list decides which partial row to read

@@ -53,6 +53,9 @@ struct CombineArgs {
   // complement pages' partials (page counts r_page_count), which refresh the cache
   const float* ro; const float* rml; int32_t r_splits; int32_t r_chunk;
   const int32_t* r_page_count;
+  // prefix-only mode over packed variable-length queries: row (b, i, h) is written to
+  // packed row cu_q[b] + i (rows with i >= cu_q[b+1] - cu_q[b] are skipped)
+  const int32_t* cu_q;
   float* cache_a; float* cache_l;      // step/LoSA cache, or prefix-only outputs
   float* ain; float* lin;              // block-only outputs
   void* a_full; int32_t out_bf16; float* l_full;
@@ -150,6 +153,9 @@ struct AppendArgs {
   int32_t tail_only;                      // in place (batch 1): write the block rows only
 };
 hipError_t launch_append(const AppendArgs& a, hipStream_t st);
+// row_tok[b][i] = the packed query row of token i of branch b (clamped into [0, total_q))
+hipError_t launch_varlen_rows(const int32_t* cu_q, int32_t batch, int32_t b_max, int32_t total_q,
+                              int32_t* row_tok, hipStream_t st);
 hipError_t launch_fill_u8(uint8_t* p, int64_t n, uint8_t value, hipStream_t st);
 hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t st);
 hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t st);

@@ -56,6 +56,28 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Multi-branch prefix pass ("Resumen Técnico: BlockBatch", system optimisation: the query
+// positions of all branches in one variable-length buffer): the row map the attention
+// kernels read queries through.  Rows past a branch's block repeat its last query (their
+// results are not written out); an empty branch points at row 0.
+__global__ void varlen_rows_kernel(const int32_t* cu_q, int batch, int b_max, int total_q, int32_t* row_tok) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)batch * b_max) return;
+  const int b = idx / b_max, i = idx % b_max;
+  const int q0 = cu_q[b], nb = cu_q[b + 1] - q0;
+  const int r = q0 + min(i, nb - 1);
+  row_tok[idx] = nb > 0 ? max(0, min(r, total_q - 1)) : 0;
+}
+
+hipError_t launch_varlen_rows(const int32_t* cu_q, int32_t batch, int32_t b_max, int32_t total_q, int32_t* row_tok,
+                              hipStream_t st) {
+  const int64_t n = (int64_t)batch * b_max;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(varlen_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, cu_q, batch, b_max,
+                     total_q, row_tok);
+  return hipGetLastError();
+}
+
 __global__ void fill_u8_kernel(uint8_t* p, int64_t n, uint8_t value) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = value;

@@ -323,6 +323,31 @@ fb_status fb_block_run(const fb_shape* s, const fb_block_plan* plan, const void*
                        float* cache_l, void* a_full_steps, float* l_full_steps, uint8_t* masks,
                        float* sims, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------------------
+ * Several branches in one prefix pass [BB, "Optimización del Sistema": the query positions
+ * of all active branches, each with its own block size and its own KV cache, packed into
+ * one variable-length buffer and processed in one pass].
+ * ------------------------------------------------------------------------------------ */
+typedef struct fb_varlen_shape {
+  fb_shape s;                  /* s.batch = branches; s.block = B_max, a bound of every
+                                  branch's block; prefixes as in fb_shape (branch b's own)  */
+  const int32_t* cu_seqlens_q; /* device [batch + 1]: branch b owns packed query rows
+                                  cu_q[b] .. cu_q[b+1]-1, cu_q[0] = 0, B_b <= B_max        */
+  int32_t total_q;             /* cu_seqlens_q[batch] (host copy; sizes the launch)        */
+} fb_varlen_shape;
+
+/* Workspace bytes for fb_prefix_attn_varlen; 0 on an invalid shape. */
+size_t fb_prefix_attn_varlen_workspace_size(const fb_varlen_shape* vs);
+
+/* Block-external pass of every branch [FB-pt §2 Mecanismo Central], one launch for all:
+ * each packed query attends to its own branch's prefix.
+ *   q [total_q][h_q][d] (dtype); a_out [total_q][h_q][d] fp32; l_out [total_q][h_q] fp32.
+ * A branch with an empty prefix gives a_out = 0, l_out = -inf; an empty branch (B_b = 0)
+ * has no rows.  total_q == 0 does nothing. */
+fb_status fb_prefix_attn_varlen(const fb_varlen_shape* vs, const void* q, const void* k,
+                                const void* v, float* a_out, float* l_out, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -215,3 +215,19 @@ def pack_selection(sel, max_sel, shuffle_seed=None):
             pages[i, h, :len(s)] = s
             count[i, h] = len(s)
     return pages, count
+
+
+def branches(seed, blocks, seqlens, h_q, h_kv, d, dtype="bf16", std=1.0) -> dict:
+    """Several branches of one request (the multi-branch pass): branch b has a block of
+    blocks[b] query positions and its own prefix of seqlens[b] tokens.  Draw order: Q
+    (packed [sum B_b, H_q, d]), K, V (packed [sum N_b, H_kv, d])."""
+    g = rng(seed)
+    bf = dtype == "bf16"
+    blocks = np.asarray(blocks, dtype=np.int64)
+    seqlens = np.asarray(seqlens, dtype=np.int64)
+    q = normal(g, (int(blocks.sum()), h_q, d), std, bf)
+    k = normal(g, (int(seqlens.sum()), h_kv, d), std, bf)
+    v = normal(g, (int(seqlens.sum()), h_kv, d), std, bf)
+    return dict(q=q, k=k, v=v, cu_q=np.concatenate([[0], np.cumsum(blocks)]).astype(np.int32),
+                cu_k=np.concatenate([[0], np.cumsum(seqlens)]).astype(np.int32), blocks=blocks, seqlens=seqlens,
+                h_q=h_q, h_kv=h_kv, d=d, dtype=dtype, scale=1.0 / float(np.sqrt(d)))

@@ -207,3 +207,20 @@ def test_lifecycle_validation():
     assert lib.fb_block_run(C.byref(s), C.byref(plan), *a3) == 3
     ls = losa_shape()
     assert lib.losa_page_meta_append(C.byref(ls), 0, f, f, f, None) == 1
+
+
+def test_varlen_validation():
+    lib = fb.load()
+    s = dllm_shape(batch=6, block=128)
+    f = C.c_void_p(0x10000)
+    vs = fb.VarlenShape(s, f, 6 * 128 + 1)                      # more rows than batch * B_max
+    assert lib.fb_prefix_attn_varlen_workspace_size(C.byref(vs)) == 0
+    vs = fb.VarlenShape(s, None, 10)
+    assert lib.fb_prefix_attn_varlen_workspace_size(C.byref(vs)) == 0
+    vs = fb.VarlenShape(s, f, 252)
+    n = lib.fb_prefix_attn_varlen_workspace_size(C.byref(vs))
+    assert n > fb.workspace_size(s)
+    assert lib.fb_prefix_attn_varlen(C.byref(vs), f, f, f, f, f, f, n - 1, None) == 3
+    assert lib.fb_prefix_attn_varlen(C.byref(vs), None, f, f, f, f, f, n, None) == 1
+    vs0 = fb.VarlenShape(s, f, 0)
+    assert lib.fb_prefix_attn_varlen(C.byref(vs0), None, None, None, None, None, None, 0, None) == 0
