@@ -431,6 +431,32 @@ def lifecycle_workload(fb, args, blocks=4, S=8):
             "prefix_final": N0 + blocks * B}
 
 
+def varlen_workload(fb, args):
+    """Multi-branch prefix pass: six branches of one request with block sizes 4, 8, 16, 32,
+    64, 128 (packed: 252 query rows) and their own prefixes of 32768 - 97 i tokens (32 heads
+    MHA, d 128, bf16, N(0,1)/sqrt(128)); one fb_prefix_attn_varlen call per step."""
+    import torch
+    import synth
+    from synth.device import tensor
+    blocks = [4, 8, 16, 32, 64, 128]
+    lens = [32768 - 97 * i for i in range(6)]
+    br = synth.branches(synth.SEED_RESIDUAL + 1, blocks, lens, 32, 32, 128, std=1.0 / np.sqrt(128.0))
+    cu_k = torch.from_numpy(br["cu_k"]).cuda()
+    cu_q = torch.from_numpy(br["cu_q"]).cuda()
+    s = fb.make_shape(6, 32, 32, 128, 128, cu_seqlens_k=cu_k, max_seqlen_k=max(lens))
+    tq = int(br["cu_q"][-1])
+    vs = fb.make_varlen_shape(s, cu_q, tq)
+    ws = torch.empty(fb.prefix_attn_varlen_workspace_size(vs), dtype=torch.uint8, device="cuda")
+    a = torch.empty((tq, 32, 128), device="cuda")
+    l = torch.empty((tq, 32), device="cuda")
+    q, k, v = tensor(br["q"]), tensor(br["k"]), tensor(br["v"])
+    steps = max(5, args.steps // 5)
+    w = wall_time(lambda tr: fb.prefix_attn_varlen(vs, q, k, v, a, l, ws), steps, 2)
+    kv = float(sum(lens)) * 32 * 128 * 2 * 2
+    return {"step_us": w * 1e6, "kv_bytes": kv, "kv_GBps": kv / w / 1e9, "frac_hbm": kv / w / 1e9 / HBM_PEAK_GBS,
+            "branches": len(blocks), "query_rows": tq, "block_sizes": blocks}
+
+
 def other_workloads(fb, args):
     import torch
     import synth
@@ -502,6 +528,8 @@ def other_workloads(fb, args):
                           "alg_bytes": meta_bytes + union_bytes,
                           "frac_hbm_step": (meta_bytes + union_bytes) / w_s / 1e9 / HBM_PEAK_GBS}
     out["sparse_residual"] = residual_workload(fb, p, dev, shape, sel, cap, steps)
+    del dev, bufs, kmin, kmax
+    out["multi_branch_varlen"] = varlen_workload(fb, args)
     return out
 
 

@@ -174,6 +174,7 @@ __device__ __forceinline__ void row_issue(const CombineArgs& C, int rowid, int l
     st.valid = i < C.cu_q[b + 1] - q0;
     st.rowid = (q0 + i) * C.h_q + h;
     st.roff = (int64_t)st.rowid * d;
+    if (!st.valid) return;   // a padded row: nothing is loaded or written
   }
   const bool has_prefix = C.mode != kModeBlockOnly;
 
