@@ -20,3 +20,14 @@ def to_device(p, device="cuda"):
         cu=torch.from_numpy(p.cu.astype(np.int32)).to(device),
     )
     return d
+
+
+def device_normal(seed: int, shape, std: float = 1.0, dtype="bf16", device="cuda"):
+    """Seeded N(0, std^2) draw made on the device (torch's Philox generator), for inputs too
+    large to draw on the host; rounded to bf16 by the dtype cast.  Both sides of a parity
+    test read the same tensor (the oracle its host copy)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn(*shape, generator=g, device=device) * std
+    return x.to(torch.bfloat16) if dtype == "bf16" else x

@@ -397,3 +397,49 @@ def test_step_threshold_equals_mask_then_step(gpu_lib):
     assert np_of(mask)[:, 0].tolist() == [1, 0, 0]
     for k_ in ("a_full", "l_full", "cache_a", "cache_l"):
         assert torch.equal(o1[k_], o2[k_]), k_
+
+
+def test_step_at_the_longest_swept_prefix(gpu_lib):
+    """The dLLM step at the longest prefix the bench sweeps (819200 tokens, 32 heads, 13.4 GB
+    of K/V in HBM): fresh, then reuse, on two sampled heads against the oracle."""
+    import torch
+    from synth.device import device_normal
+    from oracle import flashblock as OF
+    fb = gpu_lib
+    n, H, d, B = 819200, 32, 128, 32
+    std = 1.0 / np.sqrt(128.0)
+    say("[longest prefix] draw")
+    q = device_normal(71, (1, B, H, d), std)
+    k = device_normal(72, (n, H, d), std)
+    v = device_normal(73, (n, H, d), std)
+    kb = device_normal(74, (1, B, H, d), std)
+    vb = device_normal(75, (1, B, H, d), std)
+    s = fb.make_shape(1, H, H, d, B, seqlen_k=n)
+    ws = torch.empty(fb.workspace_size(s), dtype=torch.uint8, device="cuda")
+    ca = torch.zeros((1, B, H, d), device="cuda")
+    cl = torch.zeros((1, B, H), device="cuda")
+    af = torch.zeros((1, B, H, d), dtype=torch.bfloat16, device="cuda")
+    lf = torch.zeros((1, B, H), device="cuda")
+    say("[longest prefix] fresh step")
+    fb.step(s, q, k, v, kb, vb, None, ca, cl, af, lf, ws)
+    q2 = q + device_normal(76, (1, B, H, d), 0.01)
+    af2 = torch.zeros_like(af)
+    lf2 = torch.zeros_like(lf)
+    fb.step(s, q2, k, v, kb, vb, torch.ones((1, H), dtype=torch.uint8, device="cuda"), ca, cl, af2, lf2, ws)
+    torch.cuda.synchronize()
+    heads = [5, 30]
+    host = lambda t: t[..., heads, :].float().cpu().numpy().astype(np.float64)
+    qh, kh, vh, kbh, vbh, q2h = host(q), host(k), host(v), host(kb), host(vb), host(q2)
+    del k, v
+    torch.cuda.empty_cache()
+    say("[longest prefix] oracle")
+    cu = np.array([0, n], np.int32)
+    z = np.zeros((1, 2), np.uint8)
+    ea, el, na, nl = OF.step(qh, kh, vh, cu, kbh, vbh, z, None, None, 1.0 / np.sqrt(d))
+    check_attn(np_of(af)[:, :, heads], ea, "bf16", "longest fresh A_full")
+    check_lse(np_of(lf)[:, :, heads], el, "bf16", "longest fresh L_full")
+    check_attn(np_of(ca)[:, :, heads], na, "bf16", "longest cache")
+    ea2, el2, _, _ = OF.step(q2h, kh, vh, cu, kbh, vbh, np.ones((1, 2), np.uint8),
+                             np_of(ca)[:, :, heads].astype(np.float64), np_of(cl)[:, :, heads].astype(np.float64),
+                             1.0 / np.sqrt(d))
+    check_attn(np_of(af2)[:, :, heads], ea2, "bf16", "longest reuse A_full")
