@@ -88,7 +88,10 @@ bool fa_rows(const fb_shape* s, const RowPlan& rp) {
   return s->dtype == FB_BF16 && s->head_dim == 128 && rp.rows >= kFaMinRows;
 }
 #ifndef FB_FA_TARGET_ITEMS
-#define FB_FA_TARGET_ITEMS 512
+#define FB_FA_TARGET_ITEMS 512        // 8-wave items (one resident per CU): two rounds
+#endif
+#ifndef FB_FA_ITEM_OVERHEAD_KEYS
+#define FB_FA_ITEM_OVERHEAD_KEYS 256  // set-up and tail of one 4-wave item, in keys streamed
 #endif
 SplitPlan split_plan(const fb_shape* s, const RowPlan& rp, int64_t max_keys, int forced, int64_t reserved = 0) {
   SplitPlan p;
@@ -105,10 +108,27 @@ SplitPlan split_plan(const fb_shape* s, const RowPlan& rp, int64_t max_keys, int
     if (stream_rows(s, rp)) {
       want = std::max<int64_t>(1, (FB_STREAM_TARGET_ITEMS - reserved) / items);
     } else if (fa_rows(s, rp)) {
-      // resident workgroups: 2 per CU with 4 waves, 1 with 8; aim for two rounds of them
       const int64_t fa_items = (int64_t)s->batch * s->h_kv * cdiv(rp.rows, fa_rows_per_item(rp.rows));
-      const int64_t target = (fa_waves(rp.rows) == 4 ? 2 : 1) * FB_FA_TARGET_ITEMS;
-      want = std::max<int64_t>(1, (target + fa_items / 2) / fa_items);
+      if (fa_waves(rp.rows) == 4) {
+        // 4-wave (memory-bound) items, 2 resident per CU: the split count that minimises
+        // rounds of resident items x (keys per item + per-item set-up), so that the last
+        // round is not a near-empty tail and items are not needlessly short.
+        const int64_t slots = 2 * 256;
+        int64_t best = 1, best_cost = INT64_MAX;
+        for (int64_t sp = 1; sp <= 256; ++sp) {
+          const int64_t ch = std::max<int64_t>(round_up(cdiv(max_keys, sp), kTileKeys), kMinChunk);
+          if (sp > 1 && cdiv(max_keys, ch) < sp) break;   // more splits than chunks
+          const int64_t cost = cdiv(fa_items * sp, slots) * (ch + FB_FA_ITEM_OVERHEAD_KEYS);
+          if (cost < best_cost) {
+            best_cost = cost;
+            best = sp;
+          }
+        }
+        want = best;
+      } else {
+        // 8-wave (matrix-bound) items, 1 resident per CU: two rounds of them
+        want = std::max<int64_t>(1, (FB_FA_TARGET_ITEMS + fa_items / 2) / fa_items);
+      }
     } else {
       want = cdiv(kTargetItems, items);
     }
