@@ -19,7 +19,8 @@ __device__ __forceinline__ SeqInfo seq_info(const AttnSrc& S, int b, int hk, int
     r.seq0 = b * S.n_uniform;
     r.n_seq = S.n_uniform;
   }
-  r.n_keys = S.pages ? S.page_count[b * h_kv + hk] * S.page_size : r.n_seq;
+  // a page count is clamped to the list's capacity, so no key reads past the list
+  r.n_keys = S.pages ? min(S.page_count[b * h_kv + hk], S.max_union) * S.page_size : r.n_seq;
   return r;
 }
 
@@ -30,10 +31,12 @@ __device__ __forceinline__ int key_token(const AttnSrc& S, const int32_t* pg, in
   ok = key < kend;
   if (!ok) key = kend - 1;
   if (pg) {
-    int t = pg[key / S.page_size] * S.page_size + key % S.page_size;
-    if (t >= n_seq) {
+    // 64-bit: a page index outside the sequence must not wrap into it
+    const int64_t t64 = (int64_t)pg[key / S.page_size] * S.page_size + key % S.page_size;
+    int t = (int)t64;
+    if (t64 < 0 || t64 >= n_seq) {   // a page outside the sequence: skipped
       ok = false;
-      t = n_seq - 1;
+      t = n_seq > 0 ? n_seq - 1 : 0;
     }
     return t;
   }

@@ -136,8 +136,12 @@ __global__ void __launch_bounds__(64 * W, QT == 1 && W == 4 ? 2 : 1) attn_fa_ker
   const int pmask = (1 << sh) - 1;
   // Token of chunk key `key` >= kbeg, branch-free: keys past the chunk end read the last
   // staged page (the caller discards them).
+  // A page index outside [0, n_seq >> sh] gives -1 (checked before the shift, which could
+  // overflow), which every caller treats as outside the sequence.
+  const int pg_lim = si.n_seq >> sh;
   auto paged_tok = [&](int key) -> int {
-    return (pl_lds[min((key >> sh) - pbase, npl - 1)] << sh) + (key & pmask);
+    const int pg = pl_lds[min((key >> sh) - pbase, npl - 1)];
+    return (unsigned)pg <= (unsigned)pg_lim ? (pg << sh) + (key & pmask) : -1;
   };
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0, nrec, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, 0, nrec, 0x00020000);
@@ -162,7 +166,7 @@ __global__ void __launch_bounds__(64 * W, QT == 1 && W == 4 ? 2 : 1) attn_fa_ker
     _Pragma("unroll") for (int u = 0; u < NP; ++u) {                                             \
       const int key_ = kbeg + (T) * kFaTile + p_row + 4 * W * u;                                 \
       const int tok_ = paged_tok(key_);                                                          \
-      poff[u] = key_ < kend && tok_ < si.n_seq ? tok_ * (int)tstride * 2 + p_chunk * 16 : nrec; \
+      poff[u] = key_ < kend && (unsigned)tok_ < (unsigned)si.n_seq ? tok_ * (int)tstride * 2 + p_chunk * 16 : nrec; \
     }                                                                                            \
   }
 #define FA_OFF(T, U) (PAGED ? poff[U] : (T) * kFaTile * (int)tstride * 2 + g_off + (U) * g_step)
@@ -271,7 +275,7 @@ __global__ void __launch_bounds__(64 * W, QT == 1 && W == 4 ? 2 : 1) attn_fa_ker
     uint64_t vm_ = ~0ull;                                                                        \
     if constexpr (PAGED) {   /* validity of the tile's keys: lane = key */                       \
       const int key_ = kbeg + (T) * kFaTile + lane;                                              \
-      vm_ = __ballot(key_ < kend && paged_tok(key_) < si.n_seq);                                 \
+      vm_ = __ballot(key_ < kend && (unsigned)paged_tok(key_) < (unsigned)si.n_seq);             \
     }                                                                                            \
     FA_QK(acc, lds[CUR]);                                                                        \
     if (PAGED && vm_ != ~0ull) {   /* register r of half s holds key 32 s + 8 (r >> 2) + 4 g + (r & 3) */ \

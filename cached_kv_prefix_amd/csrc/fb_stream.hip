@@ -125,13 +125,16 @@ __global__ void __launch_bounds__(256, FB_STREAM_WG_PER_CU) attn_stream_kernel(c
   // Token of key `key` (ok = takes part in the softmax); p0 and pv[] are the first page of
   // the sub-tile and the indices of its (at most 3) pages.  Tokens past the resource range
   // read as zero.
+  // A page index outside [0, n_seq / P] (checked before the multiply, which could
+  // overflow) or a token past the sequence end is skipped.
+  const int pg_lim = PAGED ? si.n_seq / S.page_size : 0;
   auto tok_of = [&](int key, int p0, const int (&pv)[3], bool& ok) -> int {
     ok = key < kw1;
     if (!PAGED) return key;
     const int rel = key / S.page_size - p0;
     const int pgi = rel == 0 ? pv[0] : (rel == 1 ? pv[1] : pv[2]);
-    const int t = pgi * S.page_size + key % S.page_size;
-    ok = ok && t < si.n_seq;
+    const int t = (unsigned)pgi <= (unsigned)pg_lim ? pgi * S.page_size + key % S.page_size : -1;
+    ok = ok && (unsigned)t < (unsigned)si.n_seq;
     return t;
   };
 

@@ -245,6 +245,8 @@ size_t fb_residual_workspace_size(const fb_residual_shape* rs);
 /* One step with a cached residual.  Selection S[b][g] = sel_pages[b][g][0 .. sel_count[b][g]),
  * distinct page indices below ceil(N_b / page_size), any order (for example the
  * losa_select_union output, with max_sel = losa_union_capacity); sel_count in [0, max_sel].
+ * Indices outside [0, ceil(N_b / page_size)) are skipped, and a count above max_sel reads
+ * max_sel entries (no access leaves the list or the sequence).
  *   every row, every step: (A_s, L_s) = attention over the tokens of S of its KV head;
  *   rows of heads with reuse_mask[b][h] == 0 (refresh): (A_r, L_r) = attention over the
  *     prefix tokens outside S, written to cache_a / cache_l;

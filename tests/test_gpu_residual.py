@@ -156,3 +156,34 @@ def test_residual_full_size(gpu_lib):
                            sub(cache_l), p.scale)
     check_attn(sub(af2), ea, "bf16", "full reuse A_full")
     check_lse(sub(lf2), el, "bf16", "full reuse L_full")
+
+
+def test_out_of_range_pages_are_skipped(gpu_lib):
+    """Selections holding negative and too-large page indices, and a count above the list's
+    capacity, give the result of the valid pages alone (on the streaming, query-tiled and
+    generic paged kernels)."""
+    import torch
+    fb = gpu_lib
+    for name, hq, hkv, B, page in (("stream", 4, 4, 16, 16), ("tiled", 2, 2, 64, 16), ("generic", 4, 2, 16, 8)):
+        say(f"[residual bad pages] {name}")
+        p = synth.custom(37, 1, hq, hkv, 128, B, [700], std=1.0)
+        n_pages = -(-700 // page)
+        dev, s, rs = _shape(fb, p, page, 8)
+        good = [np.array([3, 0, n_pages - 1]), np.array([5, 2])] + [np.array([1])] * (hkv - 2)
+        pages = np.full((1, hkv, 8), -1, np.int32)
+        count = np.zeros((1, hkv), np.int32)
+        pages[0, 0, :6] = [3, -3, 0, n_pages + 7, n_pages - 1, 1 << 30]
+        count[0, 0] = 6
+        pages[0, 1, :] = [5, -1, 2, n_pages, -(1 << 30), n_pages * 3, -2, 9999]
+        count[0, 1] = 12                      # above the capacity of 8: reads 8 entries
+        for g in range(2, hkv):
+            pages[0, g, 0] = 1
+            count[0, g] = 1
+        bf = _bufs(fb, p, rs, dev)
+        _run(fb, rs, dev["q"], dev, torch.from_numpy(pages).cuda(), torch.from_numpy(count).cuda(), None, bf)
+        torch.cuda.synchronize()
+        sel = [[good[g] for g in range(hkv)]]
+        ea, el, na, nl = OR.step(p.q, p.k, p.v, p.cu, p.k_blk, p.v_blk, sel, page, np.zeros((1, hq), np.uint8),
+                                 np.zeros((1, B, hq, 128)), np.zeros((1, B, hq)), p.scale)
+        check_attn(np_of(bf["af"]), ea, "bf16", f"{name} A_full")
+        check_attn(np_of(bf["ca"]), na, "bf16", f"{name} residual")
