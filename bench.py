@@ -196,14 +196,19 @@ def flushed_step_times(fn, n=10):
 STREAM_KERNEL = "fb::attn_stream_kernel<1, 40, false>"
 
 
+# The sources the streaming kernel and its launch are built from: the kernel, the dispatch,
+# the shared device helpers and descriptors, and the host split plan.
+STREAM_SOURCES = ("fb_stream.hip", "fb_attn.hip", "fb_attn_common.hpp", "fb_device.hpp", "fb_internal.hpp",
+                  "fb_api.hip")
+
+
 def kernel_source_sha():
-    """Fingerprint of every kernel and host source the attention launch depends on."""
+    """Fingerprint of the sources the headline attention launch depends on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "cached_kv_prefix_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
-            h.update(name.encode())
-            h.update(open(os.path.join(csrc, name), "rb").read())
+    for name in STREAM_SOURCES:
+        h.update(name.encode())
+        h.update(open(os.path.join(csrc, name), "rb").read())
     return h.hexdigest()
 
 
