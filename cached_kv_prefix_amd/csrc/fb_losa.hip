@@ -11,6 +11,7 @@
 // without fused multiply-add, so the selected indices are exactly reproducible.
 #include "fb_device.hpp"
 #include "fb_internal.hpp"
+#include <type_traits>
 
 #pragma clang fp contract(off)
 
@@ -165,29 +166,51 @@ __global__ void __launch_bounds__(256) active_kernel(const LosaArgs a, const dou
   }
 }
 
-// QUEST page scores.  grid (page blocks of 256 * QPP, h_kv, batch); a thread scores QPP
-// pages for the active rows of the KV head's query heads, 8 rows at a time.  With
-// q+ = max(q, 0) and q- = min(q, 0) (held in LDS as fp64 pairs),
+// QUEST page scores.  grid (page blocks of 128 * kQpp, h_kv, batch), 256 threads.  Lane l
+// of wave w scores pages ((blockIdx.x * 4 + w) * 32 + (l & 31)) * kQpp + 0 .. kQpp-1 for rows
+// 4 (l >> 5) .. 4 (l >> 5) + 3 of the current chunk of 8 active rows, so the two halves of a
+// wave read the same metadata (one fetch) and each fp64 pair of q read from LDS feeds
+// 2 kQpp FMAs.  With q+ = max(q, 0) and q- = min(q, 0) (held in LDS as fp64 pairs),
 //   acc + q * (q >= 0 ? kmax : kmin) == fma(q-, kmin, fma(q+, kmax, acc))
 // exactly: one of the two products is zero, the other is exact in fp64 and rounds once, as
 // in the left-to-right fp64 sum over d of the definition.
-constexpr int kQpp = 2;
+constexpr int kQpp = 4;
+constexpr int kQRow = 257;   // LDS row stride (pairs): the two half-waves' rows fall in different banks
+template <bool BF16>
 __global__ void __launch_bounds__(256) quest_score_kernel(const LosaArgs a, const void* qc, const int32_t* active,
                                                           const void* kmin, const void* kmax, double* scores) {
-  __shared__ __attribute__((aligned(16))) double qpn[8][256][2];
+  __shared__ __attribute__((aligned(16))) double qpn[8][kQRow][2];
   const int b = blockIdx.z, hk = blockIdx.y;
-  const int p0 = (blockIdx.x * 256 + threadIdx.x) * kQpp;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, rg = lane >> 5;
+  const int p0 = ((blockIdx.x * 4 + w) * 32 + (lane & 31)) * kQpp;
   int seq0, n;
   seq_of(a, b, seq0, n);
   const int P = (n + a.page_size - 1) / a.page_size;
   const int d = a.d, nc = d / 8;
   const int R = a.G * a.n_active;
   const int64_t mbase = (((int64_t)b * a.h_kv + hk) * nc) * a.max_pages * 8;
+  // Metadata of chunk c for this thread's pages (clamped to the last page: always in range),
+  // kept raw (bf16: one 16-byte vector per page) and widened where it is used.
+  typedef float f32x8 __attribute__((ext_vector_type(8)));
+  typedef typename std::conditional<BF16, u32x4, f32x8>::type Raw;
+  auto load_meta = [&](const void* m, int c, int u) -> Raw {
+    const int64_t off = mbase + ((int64_t)c * a.max_pages + min(p0 + u, P - 1)) * 8;
+    if constexpr (BF16)
+      return *(const u32x4*)((const uint16_t*)m + off);
+    else
+      return *(const f32x8*)((const float*)m + off);
+  };
+  auto elem = [&](const Raw& x, int e) -> double {
+    if constexpr (BF16)
+      return (double)__uint_as_float((e & 1) ? (x[e >> 1] & 0xffff0000u) : (x[e >> 1] << 16));
+    else
+      return (double)x[e];
+  };
   for (int r0 = 0; r0 < R; r0 += 8) {
     const int nr = min(8, R - r0);
     __syncthreads();
-    for (int w = threadIdx.x; w < 8 * d; w += 256) {
-      const int rr = w / d, j = w % d;
+    for (int t = threadIdx.x; t < 8 * d; t += 256) {
+      const int rr = t / d, j = t % d;
       double q = 0.0;
       if (rr < nr) {
         const int r = r0 + rr;
@@ -200,46 +223,54 @@ __global__ void __launch_bounds__(256) quest_score_kernel(const LosaArgs a, cons
     }
     __syncthreads();
     if (p0 >= P) continue;
-    double acc[kQpp][8];
+    double acc[kQpp][4];
 #pragma unroll
     for (int u = 0; u < kQpp; ++u)
 #pragma unroll
-      for (int rr = 0; rr < 8; ++rr) acc[u][rr] = 0.0;
+      for (int rr = 0; rr < 4; ++rr) acc[u][rr] = 0.0;
+    Raw mn[kQpp], mx[kQpp];
+#pragma unroll
+    for (int u = 0; u < kQpp; ++u) {
+      mn[u] = load_meta(kmin, 0, u);
+      mx[u] = load_meta(kmax, 0, u);
+    }
     for (int c = 0; c < nc; ++c) {
-      double kn[kQpp][8], kx[kQpp][8];
+      Raw cn[kQpp], cx[kQpp];
 #pragma unroll
       for (int u = 0; u < kQpp; ++u) {
-        const int64_t off = mbase + ((int64_t)c * a.max_pages + min(p0 + u, P - 1)) * 8;
-        if (a.bf16) {
-          const u16x8 vn = *(const u16x8*)((const uint16_t*)kmin + off);
-          const u16x8 vx = *(const u16x8*)((const uint16_t*)kmax + off);
+        cn[u] = mn[u];
+        cx[u] = mx[u];
+      }
+      if (c + 1 < nc) {   // the next chunk's metadata is in flight while this one is scored
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            kn[u][e] = (double)bf16_to_f32(vn[e]);
-            kx[u][e] = (double)bf16_to_f32(vx[e]);
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            kn[u][e] = (double)((const float*)kmin)[off + e];
-            kx[u][e] = (double)((const float*)kmax)[off + e];
-          }
+        for (int u = 0; u < kQpp; ++u) {
+          mn[u] = load_meta(kmin, c + 1, u);
+          mx[u] = load_meta(kmax, c + 1, u);
         }
       }
 #pragma unroll
-      for (int rr = 0; rr < 8; ++rr)
+      for (int e = 0; e < 8; ++e) {
+        double kn[kQpp], kx[kQpp];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const double qp_ = qpn[rr][c * 8 + e][0], qn_ = qpn[rr][c * 8 + e][1];
-#pragma unroll
-          for (int u = 0; u < kQpp; ++u) acc[u][rr] = __builtin_fma(qn_, kn[u][e], __builtin_fma(qp_, kx[u][e], acc[u][rr]));
+        for (int u = 0; u < kQpp; ++u) {
+          kn[u] = elem(cn[u], e);
+          kx[u] = elem(cx[u], e);
         }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const double qp_ = qpn[4 * rg + rr][c * 8 + e][0], qn_ = qpn[4 * rg + rr][c * 8 + e][1];
+#pragma unroll
+          for (int u = 0; u < kQpp; ++u) acc[u][rr] = __builtin_fma(qn_, kn[u], __builtin_fma(qp_, kx[u], acc[u][rr]));
+        }
+      }
     }
 #pragma unroll
     for (int u = 0; u < kQpp; ++u) {
       if (p0 + u >= P) continue;
-      for (int rr = 0; rr < nr; ++rr) {
-        const int r = r0 + rr;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        if (4 * rg + rr >= nr) continue;
+        const int r = r0 + 4 * rg + rr;
         const int h = hk * a.G + r / a.n_active;
         const int ai = r % a.n_active;
         scores[(((int64_t)b * a.h_q + h) * a.n_active + ai) * a.max_pages + p0 + u] = acc[u][rr];
@@ -279,7 +310,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const LosaArgs a, const doubl
   constexpr int NW = 4 * KPT;                   // 64-page words of the bitmaps
   __shared__ int hist[256];
   __shared__ int tmp[4];
-  __shared__ int s_digit, s_above;
+  __shared__ int s_digit, s_above, s_count;
   __shared__ unsigned long long s_and, s_or;
   __shared__ uint64_t gt_bits[NW], eq_bits[NW];
   const int rid = blockIdx.x;                   // (b * h_q + h) * n_active + ai
@@ -358,18 +389,25 @@ __global__ void __launch_bounds__(256) topk_kernel(const LosaArgs a, const doubl
     if (cum >= need && cum - c < need) {
       s_digit = 255 - tid;
       s_above = cum - c;
+      s_count = c;
     }
     __syncthreads();
     need -= s_above;
     prefix |= (uint64_t)s_digit << shift;
     pmask |= (uint64_t)255 << shift;
+    const bool whole = s_count == need;          // the bucket is exactly what is still needed
     __syncthreads();
+    if (whole) break;
   }
-  const uint64_t T = prefix;                    // the k-th largest key; `need` equal keys go in
+  // Selected: keys above the bucket (prefix bits greater) and `need` keys of the bucket,
+  // lowest pages first (the whole bucket when the passes stopped early; equal full keys
+  // otherwise).
+  const uint64_t T = prefix;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const bool valid = tid + 256 * j < P;
-    const uint64_t g = __ballot(valid && key[j] > T), e = __ballot(valid && key[j] == T);
+    const uint64_t km = key[j] & pmask;
+    const uint64_t g = __ballot(valid && km > T), e = __ballot(valid && km == T);
     if (lane == 0) {
       gt_bits[4 * j + w] = g;
       eq_bits[4 * j + w] = e;
@@ -456,8 +494,11 @@ hipError_t launch_locality(const LosaArgs& a, const void* qc, const void* qp, do
 
 hipError_t launch_quest_scores(const LosaArgs& a, const void* qc, const int32_t* active, const void* kmin,
                                const void* kmax, double* scores, hipStream_t st) {
-  dim3 grid((unsigned)((a.max_pages + 256 * kQpp - 1) / (256 * kQpp)), a.h_kv, a.batch);
-  hipLaunchKernelGGL(quest_score_kernel, grid, dim3(256), 0, st, a, qc, active, kmin, kmax, scores);
+  dim3 grid((unsigned)((a.max_pages + 128 * kQpp - 1) / (128 * kQpp)), a.h_kv, a.batch);
+  if (a.bf16)
+    hipLaunchKernelGGL(quest_score_kernel<true>, grid, dim3(256), 0, st, a, qc, active, kmin, kmax, scores);
+  else
+    hipLaunchKernelGGL(quest_score_kernel<false>, grid, dim3(256), 0, st, a, qc, active, kmin, kmax, scores);
   return hipGetLastError();
 }
 
