@@ -306,6 +306,7 @@ fb_status fb_lse_merge(int64_t rows, int32_t d, const float* a_out, const float*
                        const float* l_in, void* a_full, fb_dtype out_dtype, float* l_full, hipStream_t stream) {
   if (rows < 0 || d < 1 || d > 256) return rows < 0 || d < 1 ? FB_ERR_INVALID_ARG : FB_ERR_UNSUPPORTED;
   if (out_dtype != FB_BF16 && out_dtype != FB_F32) return FB_ERR_INVALID_ARG;
+  if (rows > 4 * (int64_t)INT32_MAX) return FB_ERR_UNSUPPORTED;   // four rows per workgroup
   if (rows == 0) return FB_OK;
   if (!a_out || !l_out || !a_in || !l_in || !a_full) return FB_ERR_INVALID_ARG;
   return hip_status(launch_lse_merge(rows, d, a_out, l_out, a_in, l_in, a_full, out_dtype == FB_BF16, l_full, stream));
@@ -367,17 +368,20 @@ fb_status fb_step_threshold(const fb_shape* s, const void* q, const void* k, con
 fb_status fb_mask_threshold(const int32_t* m_updated, int32_t tau, int32_t batch, int32_t h_q, uint8_t* mask,
                             hipStream_t stream) {
   if (!m_updated || !mask || batch < 1 || h_q < 1) return FB_ERR_INVALID_ARG;
+  if ((int64_t)batch * h_q > ((int64_t)INT32_MAX << 8)) return FB_ERR_UNSUPPORTED;
   return hip_status(launch_mask_threshold(m_updated, tau, batch, h_q, mask, stream));
 }
 
 fb_status fb_mask_similarity(const float* sim, float gamma, int64_t n, uint8_t* mask, hipStream_t stream) {
   if (n < 0 || (n > 0 && (!sim || !mask))) return FB_ERR_INVALID_ARG;
+  if (n > ((int64_t)INT32_MAX << 8)) return FB_ERR_UNSUPPORTED;
   return hip_status(launch_mask_similarity(sim, gamma, n, mask, stream));
 }
 
 fb_status fb_head_cosine(int32_t batch, int32_t block, int32_t h_q, int32_t head_dim, const float* a_prev,
                          const float* a_cur, float* sim, hipStream_t stream) {
   if (batch < 1 || block < 1 || h_q < 1 || head_dim < 1 || !a_prev || !a_cur || !sim) return FB_ERR_INVALID_ARG;
+  if ((int64_t)batch * h_q > INT32_MAX) return FB_ERR_UNSUPPORTED;   // one workgroup per (b, h)
   return hip_status(launch_head_cosine(batch, block, h_q, head_dim, a_prev, a_cur, sim, stream));
 }
 
@@ -396,6 +400,7 @@ fb_status check_losa(const losa_shape* ls) {
   if (ls->page_size < 1 || ls->topk < 1 || ls->n_active < 1 || ls->max_pages < 1) return FB_ERR_INVALID_ARG;
   if (ls->n_active > s.block) return FB_ERR_INVALID_ARG;
   if (s.block > 1024 || ls->max_pages > 16384 || s.head_dim % 8 != 0 || s.h_q > 1024) return FB_ERR_UNSUPPORTED;
+  if ((int64_t)s.batch * s.h_q * ls->n_active > INT32_MAX) return FB_ERR_UNSUPPORTED;   // top-k grid
   if (cdiv(max_prefix(&s), ls->page_size) > ls->max_pages) return FB_ERR_INVALID_ARG;
   return FB_OK;
 }

@@ -224,3 +224,16 @@ def test_varlen_validation():
     assert lib.fb_prefix_attn_varlen(C.byref(vs), None, f, f, f, f, f, n, None) == 1
     vs0 = fb.VarlenShape(s, f, 0)
     assert lib.fb_prefix_attn_varlen(C.byref(vs0), None, None, None, None, None, None, 0, None) == 0
+
+
+def test_grid_size_limits_are_rejected_before_launch():
+    """Sizes whose launch grid would not fit return FB_ERR_UNSUPPORTED instead of wrapping."""
+    lib = fb.load()
+    f = C.c_void_p(0x10000)
+    assert lib.fb_lse_merge(1 << 34, 128, f, f, f, f, f, 0, None, None) == 2
+    assert lib.fb_mask_similarity(f, 0.9, 1 << 40, f, None) == 2
+    assert lib.fb_mask_threshold(f, 4, 1 << 30, 1 << 10, f, None) == 2
+    assert lib.fb_head_cosine(1 << 16, 4, 1 << 16, 128, f, f, f, None) == 2
+    ls = fb.make_losa_shape(fb.make_shape(65535, 1024, 1024, 128, 1024, seqlen_k=16), page_size=16, topk=1,
+                            n_active=1024, max_pages=1)
+    assert fb.losa_workspace_size(ls) == 0
