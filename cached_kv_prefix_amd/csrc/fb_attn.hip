@@ -1,5 +1,6 @@
-// Split-KV attention partials for the FlashBlock prefix pass, the block pass and the
-// LoSA sparse prefix pass.
+// Split-KV attention partials: the generic kernels behind the streaming and query-tiled
+// ones (bf16 with d = 64, fp32 inputs, paged sources with pages of fewer than 16 tokens
+// or groups of more than 128 rows) and the dispatch between the three.
 //
 // What is computed ("Resumo Técnico: FlashBlock", §2 Mecanismo Central; "LoSA", §2 step 3):
 // for every query row of a (sequence, KV head) group and one contiguous chunk of that

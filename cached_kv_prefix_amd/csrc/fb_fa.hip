@@ -1,25 +1,31 @@
 // Query-tiled attention for query groups of more than 32 rows: the video-sized block and
-// its prefix pass (4680 rows per head, a dense contraction bound by the matrix cores) and
-// grouped-query prefixes (4 query heads x 32 block tokens share each K / V tile).  Same split-KV partial-result format as the other
-// attention kernels; fb_combine.hip reduces the chunks and merges.
+// its prefix pass (4680 rows per head, a dense contraction bound by the matrix cores),
+// grouped-query prefixes (4 query heads x 32 block tokens share each K / V tile), 64-row
+// blocks, the paged selected / complement passes of the sparse-residual step and the
+// multi-branch pass.  Same split-KV partial-result format as the other attention
+// kernels; fb_combine.hip reduces the chunks and merges.
 //
 // What is computed ("Resumo Técnico: FlashBlock", §2 Mecanismo Central): for the query
 // rows of one (sequence, KV head) group and one key chunk, base-2 running statistics
 //   m = max_j s_j,  l = sum_j 2^(s_j - m),  O = sum_j 2^(s_j - m) v_j,  s_j = log2(e) scale <q, k_j>.
 //
 // gfx950 design:
-//   * a workgroup = W waves owns 32 * W * QT query rows (W = 4 for groups of up to 128
-//     rows, such as 4 query heads x 32 block tokens, else 8); a wave owns 32 * QT rows (QT
-//     query tiles), so every K / V operand read from LDS feeds QT matrix instructions;
+//   * a workgroup = W waves owns 32 * W * QT query rows (QT = 1); a wave owns 32 * QT rows;
 //   * keys advance in 64-key tiles, double-buffered in LDS and shared by the W waves: the
-//     next tiles are loaded into registers (16-byte
-//     row pieces, buffer loads) while the current one is computed, then written to the
-//     other LDS buffer; one barrier per tile;
-//   * software pipeline: S of tile t + 1 is issued before the softmax of tile t, so the
-//     matrix instructions and the vector softmax of one wave are independent.  Measured on
-//     MI355X: the matrix core and the vector ALU of one SIMD overlap only partly within a
-//     wave and not across waves, so the softmax (about half the matrix time) mostly adds to
-//     it; the kernel reaches about 40% of the bf16 peak, the matrix work alone 85%;
+//     next tiles are loaded into registers (16-byte row pieces, buffer loads) while the
+//     current one is computed, then written to the other LDS buffer; one barrier per tile;
+//   * groups of more than 128 rows (W = 8, matrix-bound): software pipeline, S of tile
+//     t + 1 is issued before the softmax of tile t, so the matrix instructions and the
+//     vector softmax of one wave are independent.  Measured on MI355X: the matrix core
+//     and the vector ALU of one SIMD overlap only partly within a wave and not across
+//     waves, so the softmax (about half the matrix time) mostly adds to it; the kernel
+//     reaches about 40% of the bf16 peak, the matrix work alone 85%;
+//   * groups of 33-128 rows (W = 4, DEEP, memory-bound): no score pipelining, two tiles of
+//     loads in flight (two register staging sets);
+//   * a paged source (DEEP only, power-of-two pages): the chunk's page list is staged in
+//     LDS once; each load piece computes its token offset without branches, and a key
+//     past the chunk or a token outside the sequence gets an out-of-range offset (reads
+//     zero) and is masked by the tile's validity ballot;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K rows chunk-swizzled by key & 15 for
 //     conflict-free ds_read_b128); softmax in registers, one query per lane; O^T = V^T P^T
 //     with V^T from ds_read_b64_tr_b16 (V rows swizzled by key & 3);
@@ -27,9 +33,6 @@
 //     they are the long ones, so the short block items fill in behind them.
 #include "fb_attn_common.hpp"
 
-#ifndef FB_FA_BIG
-#define FB_FA_BIG 0
-#endif
 
 namespace fb {
 
@@ -440,10 +443,6 @@ hipError_t launch_fa(const AttnArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((attn_fa_kernel<kFaQt, 4, true, true>), dim3((unsigned)n), dim3(256), 0, st, a);
   else if (fa_waves(rows) == 4)
     hipLaunchKernelGGL((attn_fa_kernel<kFaQt, 4, true, false>), dim3((unsigned)n), dim3(256), 0, st, a);
-  else if (FB_FA_BIG == 1)
-    hipLaunchKernelGGL((attn_fa_kernel<2, 4, true, false>), dim3((unsigned)n), dim3(256), 0, st, a);
-  else if (FB_FA_BIG == 2)
-    hipLaunchKernelGGL((attn_fa_kernel<2, 4, false, false>), dim3((unsigned)n), dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((attn_fa_kernel<kFaQt, 8, false, false>), dim3((unsigned)n), dim3(512), 0, st, a);
   return hipGetLastError();

@@ -1,6 +1,7 @@
 // Streaming split-KV attention for query groups of at most 32 rows (the FlashBlock
-// prefix pass of a dLLM block, the block pass at small B, and the LoSA sparse pass over
-// the union pages).  Same partial-result format as fb_attn.hip.
+// prefix pass of a dLLM block, the block pass at small B, the LoSA sparse pass over the
+// union pages, and the selected / complement page passes of the sparse-residual step).
+// Same partial-result format as fb_attn.hip.
 //
 // What is computed ("Resumo Técnico: FlashBlock", §2 Mecanismo Central; "LoSA", §2 step 3):
 // for one (sequence, KV head) group and one key chunk, base-2 running statistics
@@ -22,9 +23,9 @@
 //     loads at their use, which drains the pipeline;
 //   * the sub-tile sequence is straight-line code (TMAX steps, each entered only after
 //     the previous one, with a uniform early exit) and every step issues the same loads
-//     (past the end they re-read one clamped, cache-resident row), so the compiler's
-//     wait counts keep NS-1 sub-tiles outstanding; a loop back-edge would make it drain
-//     all outstanding loads at the loop head;
+//     (past the end they fall outside the buffer resource and return zero without a
+//     fetch), so the compiler's wait counts keep NS-1 sub-tiles outstanding; a loop
+//     back-edge would make it drain all outstanding loads at the loop head;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: the K operand is read from LDS with
 //     ds_read_b128 (K rows stored with their 16-byte chunks XOR-swizzled by key & 15, so
 //     16 keys of one chunk hit distinct banks); a lane holds one query and 16 keys, so
@@ -33,13 +34,11 @@
 //     ds_read_b64_tr_b16, which hands each lane 4 keys of its own V column.  V rows are
 //     stored with their 16-byte chunks XOR-swizzled by (key & 3) so the four rows of one
 //     transposed read fall in distinct LDS banks;
-//   * a paged source (LoSA union, page size >= 16) reads the wave-uniform page indices of
-//     a sub-tile with scalar loads, which do not queue behind the vector loads.
+//   * a paged source (page size >= 16) reads the wave-uniform page indices of a sub-tile
+//     with scalar loads, which do not queue behind the vector loads; a page index outside
+//     the sequence is skipped.
 #include "fb_attn_common.hpp"
 
-#ifndef FB_STREAM_SRC1_FIRST
-#define FB_STREAM_SRC1_FIRST 0
-#endif
 #ifndef FB_STREAM_WG_PER_CU
 #define FB_STREAM_WG_PER_CU 1
 #endif
@@ -352,11 +351,6 @@ hipError_t launch_stream(const AttnArgs& a, hipStream_t st) {
     return hipErrorInvalidValue;
   if (paged) {
     hipLaunchKernelGGL((attn_stream_kernel<kStreamDepth, kStreamTmax, true>), grid, dim3(256), 0, st, a);
-  } else if (FB_STREAM_SRC1_FIRST && a.src1.n_splits) {
-    AttnArgs sw = a;
-    sw.src0 = a.src1;
-    sw.src1 = a.src0;
-    hipLaunchKernelGGL((attn_stream_kernel<kStreamDepth, kStreamTmax, false>), grid, dim3(256), 0, st, sw);
   } else {
     hipLaunchKernelGGL((attn_stream_kernel<kStreamDepth, kStreamTmax, false>), grid, dim3(256), 0, st, a);
   }
