@@ -83,6 +83,12 @@ PREFIX_CASES = [
     ("rows300_mha", 1, 2, 2, 128, 300, [1000], "bf16"),
     ("rows400_gqa2", 1, 4, 2, 128, 200, [777], "bf16"),
     ("rows260_varlen_empty", 2, 2, 1, 128, 130, [0, 2100], "bf16"),
+    ("rows33_first_tiled", 1, 1, 1, 128, 33, [1500], "bf16"),
+    ("rows128_deep_edge", 1, 2, 2, 128, 128, [900], "bf16"),
+    ("rows129_wide_edge", 1, 1, 1, 128, 129, [900], "bf16"),
+    ("B1_mqa_g32", 2, 32, 1, 128, 1, [2000, 5], "bf16"),
+    ("d64_rows64_generic", 1, 4, 1, 64, 16, [800], "bf16"),
+    ("one_full_stream_chunk", 1, 2, 2, 128, 32, [5120], "bf16"),
     ("f32_d64", 2, 2, 2, 64, 4, [60, 77], "f32"),
     ("f32_d128_gqa", 1, 4, 2, 128, 7, [300], "f32"),
 ]
