@@ -316,7 +316,8 @@ namespace {
 fb_status run_step(const fb_shape* s, const void* q, const void* k, const void* v, const void* k_blk,
                    const void* v_blk, const uint8_t* reuse_mask, const int32_t* m_upd, int32_t tau,
                    float* cache_a, float* cache_l, void* a_full, float* l_full, void* ws, size_t ws_bytes,
-                   const fb_trace* trace, hipStream_t stream) {
+                   const fb_trace* trace, hipStream_t stream, double* sim_parts = nullptr,
+                   uint8_t* mask_out = nullptr) {
   fb_status st = check_shape(s);
   if (st != FB_OK) return st;
   if ((st = check_inputs(s, q, k, v)) != FB_OK) return st;
@@ -342,6 +343,8 @@ fb_status run_step(const fb_shape* s, const void* q, const void* k, const void* 
   c.cache_l = cache_l;
   c.a_full = a_full;
   c.l_full = l_full;
+  c.sim_parts = sim_parts;
+  c.mask_out = mask_out;
   rec(trace ? trace->merge_begin : nullptr, stream);
   if (hipError_t e = launch_combine(c, stream)) return hip_status(e);
   rec(trace ? trace->merge_end : nullptr, stream);
@@ -730,13 +733,13 @@ inline size_t el_size(const fb_shape* s) { return s->dtype == FB_BF16 ? 2 : 4; }
 
 struct BlockPlan {
   StepPlan step;
-  size_t prev_off, sim_off, ws_bytes;
+  size_t parts_off, sim_off, ws_bytes;
 };
 BlockPlan block_plan(const fb_shape* s) {
   BlockPlan p;
   p.step = step_plan(s);
-  p.prev_off = align256(p.step.ws_bytes);
-  p.sim_off = align256(p.prev_off + (size_t)s->batch * s->block * s->h_q * s->head_dim * sizeof(float));
+  p.parts_off = align256(p.step.ws_bytes);   // per-row cosine sums, written by the step's combine
+  p.sim_off = align256(p.parts_off + (size_t)s->batch * s->block * s->h_q * 3 * sizeof(double));
   p.ws_bytes = align256(p.sim_off + (size_t)s->batch * s->h_q * sizeof(float));
   return p;
 }
@@ -813,39 +816,42 @@ fb_status fb_block_run(const fb_shape* s, const fb_block_plan* plan, const void*
   const size_t el = el_size(s);
   // every step's operands stay 16-byte aligned
   if ((q_elems * el) % 16 != 0 || (kb_elems * el) % 16 != 0) return FB_ERR_UNSUPPORTED;
-  float* prev = (float*)((char*)ws + p.prev_off);
+  double* parts = (double*)((char*)ws + p.parts_off);
   float* sim_ws = (float*)((char*)ws + p.sim_off);
   const bool cos_needed = plan->rule == FB_RULE_SIMILARITY || sims != nullptr;
-  const float* sim_prev = nullptr;
+  // Per step: the attention and combine launches of fb_step (the combine records the
+  // decision it applied in masks[step]); with a similarity, the reduction of the per-row
+  // cosine sums the combine wrote, which also writes the next step's per-head mask.
   for (int step = 0; step < plan->n_steps; ++step) {
     uint8_t* m = masks + step * bh;
-    hipError_t e;
-    if (plan->rule == FB_RULE_THRESHOLD)
-      e = step == 0 ? launch_fill_u8(m, bh, 0, stream)
-                    : launch_mask_threshold(m_steps + (int64_t)step * s->batch, plan->tau, s->batch, s->h_q, m, stream);
-    else
-      e = step < 2 ? launch_fill_u8(m, bh, 0, stream) : launch_mask_similarity(sim_prev, plan->gamma, bh, m, stream);
-    if (e != hipSuccess) return hip_status(e);
-    if (cos_needed && step >= 1)
-      if ((e = launch_copy_f32(cache_a, prev, q_elems, stream)) != hipSuccess) return hip_status(e);
+    const uint8_t* mask_in = nullptr;   // null and no count: every head refreshes
+    const int32_t* m_upd = nullptr;
+    uint8_t* mask_out = m;
+    if (plan->rule == FB_RULE_THRESHOLD && step >= 1) {
+      m_upd = m_steps + (int64_t)step * s->batch;   // M < tau, evaluated in the step's kernels
+    } else if (plan->rule == FB_RULE_SIMILARITY && step >= 2) {
+      mask_in = m;                                  // written by the previous step's reduction
+      mask_out = nullptr;
+    }
     const char* qs = (const char*)q_steps + step * q_elems * el;
     const char* kbs = (const char*)k_blk_steps + step * kb_elems * el;
     const char* vbs = (const char*)v_blk_steps + step * kb_elems * el;
     char* af = (char*)a_full_steps + step * q_elems * el;
     float* lf = l_full_steps ? l_full_steps + step * bh * s->block : nullptr;
-    st = run_step(s, qs, k, v, kbs, vbs, m, nullptr, 0, cache_a, cache_l, af, lf, ws, p.step.ws_bytes, nullptr,
-                  stream);
+    st = run_step(s, qs, k, v, kbs, vbs, mask_in, m_upd, plan->tau, cache_a, cache_l, af, lf, ws, p.step.ws_bytes,
+                  nullptr, stream, cos_needed && step >= 1 ? parts : nullptr, mask_out);
     if (st != FB_OK) return st;
-    float* sim_s = sims ? sims + step * bh : sim_ws;
     if (cos_needed) {
+      float* sim_s = sims ? sims + step * bh : sim_ws;
+      hipError_t e;
       if (step == 0) {
         if (sims && (e = launch_fill_f32(sim_s, bh, __builtin_nanf(""), stream)) != hipSuccess) return hip_status(e);
-      } else if ((e = launch_head_cosine(s->batch, s->block, s->h_q, s->head_dim, prev, cache_a, sim_s, stream)) !=
-                 hipSuccess) {
-        return hip_status(e);
+      } else {
+        uint8_t* next = plan->rule == FB_RULE_SIMILARITY && step + 1 < plan->n_steps ? masks + (step + 1) * bh : nullptr;
+        if ((e = launch_sim_reduce(s->batch, s->block, s->h_q, parts, sim_s, plan->gamma, next, stream)) != hipSuccess)
+          return hip_status(e);
       }
     }
-    sim_prev = sim_s;
   }
   return FB_OK;
 }

@@ -96,6 +96,34 @@ __global__ void __launch_bounds__(256) head_cosine_kernel(int B, int h_q, int d,
   }
 }
 
+// One thread per (b, h): the head's rows in order, then the cosine (0 for a zero vector);
+// with next_mask, also the per-head rule for the next step (sim > gamma, fp32).
+__global__ void sim_reduce_kernel(int batch, int B, int h_q, const double* parts, float* sim, float gamma,
+                                  uint8_t* next_mask) {
+  const int64_t bh = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (bh >= (int64_t)batch * h_q) return;
+  const int h = bh % h_q, b = bh / h_q;
+  double xy = 0.0, xx = 0.0, yy = 0.0;
+  for (int i = 0; i < B; ++i) {
+    const double* p = parts + (((int64_t)b * B + i) * h_q + h) * 3;
+    xy += p[0];
+    xx += p[1];
+    yy += p[2];
+  }
+  const float s = (xx == 0.0 || yy == 0.0) ? 0.f : (float)(xy / (sqrt(xx) * sqrt(yy)));
+  sim[bh] = s;
+  if (next_mask) next_mask[bh] = s > gamma ? 1 : 0;
+}
+
+hipError_t launch_sim_reduce(int32_t batch, int32_t B, int32_t h_q, const double* parts, float* sim,
+                             float gamma, uint8_t* next_mask, hipStream_t st) {
+  const int64_t n = (int64_t)batch * h_q;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(sim_reduce_kernel, dim3((unsigned)((n + 63) / 64)), dim3(64), 0, st, batch, B, h_q, parts, sim,
+                     gamma, next_mask);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const CombineArgs& c, hipStream_t st) {
   const int64_t rows = (int64_t)c.batch * c.B * c.h_q;
   if (rows == 0) return hipSuccess;

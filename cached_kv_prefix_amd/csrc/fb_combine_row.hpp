@@ -245,6 +245,29 @@ __device__ __forceinline__ void row_finish(const CombineArgs& C, int lane, const
       lo = st.cached_l;
     }
     if (C.mode == kModePrefixOnly) return;
+    if (C.mask_out && st.i == 0 && lane == 0) C.mask_out[st.b * C.h_q + st.h] = st.fresh ? 0 : 1;
+    if (C.sim_parts) {   // the row's share of the head's cosine between the cache before and after
+      double xy = 0.0, xx = 0.0, yy = 0.0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const double x = st.cached[e], y = ao[e];   // lanes past d hold zeros
+        xy += x * y;
+        xx += x * x;
+        yy += y * y;
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        xy += __shfl_xor(xy, o);
+        xx += __shfl_xor(xx, o);
+        yy += __shfl_xor(yy, o);
+      }
+      if (lane == 0) {
+        double* sp = C.sim_parts + (int64_t)st.rowid * 3;
+        sp[0] = xy;
+        sp[1] = xx;
+        sp[2] = yy;
+      }
+    }
   }
 
   // block-internal part

@@ -56,6 +56,11 @@ struct CombineArgs {
   // prefix-only mode over packed variable-length queries: row (b, i, h) is written to
   // packed row cu_q[b] + i (rows with i >= cu_q[b+1] - cu_q[b] are skipped)
   const int32_t* cu_q;
+  // step mode: per row, the fp64 sums <old, new>, |old|^2, |new|^2 of the cached A_out
+  // before and after the step ([batch][B][h_q][3]), or null
+  double* sim_parts;
+  // step mode: the reuse decision of every (b, h) is recorded here (1 = reused), or null
+  uint8_t* mask_out;
   float* cache_a; float* cache_l;      // step/LoSA cache, or prefix-only outputs
   float* ain; float* lin;              // block-only outputs
   void* a_full; int32_t out_bf16; float* l_full;
@@ -107,6 +112,9 @@ hipError_t launch_mask_similarity(const float* sim, float gamma, int64_t n, uint
                                   hipStream_t st);
 hipError_t launch_head_cosine(int32_t batch, int32_t B, int32_t h_q, int32_t d,
                               const float* a0, const float* a1, float* sim, hipStream_t st);
+// sim[b][h] from the per-row sums the step's combine wrote (rows in order)
+hipError_t launch_sim_reduce(int32_t batch, int32_t B, int32_t h_q, const double* parts, float* sim,
+                             float gamma, uint8_t* next_mask, hipStream_t st);
 
 // LoSA selection
 struct LosaArgs {
@@ -158,6 +166,5 @@ hipError_t launch_varlen_rows(const int32_t* cu_q, int32_t batch, int32_t b_max,
                               int32_t* row_tok, hipStream_t st);
 hipError_t launch_fill_u8(uint8_t* p, int64_t n, uint8_t value, hipStream_t st);
 hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t st);
-hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t st);
 
 }  // namespace fb

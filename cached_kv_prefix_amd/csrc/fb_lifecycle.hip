@@ -1,6 +1,6 @@
-// Block lifecycle kernels: append a finished block's K/V to the packed prefix, and the
-// small fills and copies the block driver needs (kernels rather than memset nodes, so a
-// captured step sequence holds kernel nodes only).
+// Block lifecycle kernels: append a finished block's K/V to the packed prefix, the row map
+// of the multi-branch pass, and the small fills the block driver needs (kernels rather than
+// memset nodes, so a captured step sequence holds kernel nodes only).
 //
 // "FlashBlock: Attention Caching for Efficient Long-Context Block Diffusion", abstract:
 // block-wise causal inference over a KV cache that grows block by block.  Once a block's
@@ -88,14 +88,6 @@ __global__ void fill_f32_kernel(float* p, int64_t n, float value) {
   if (i < n) p[i] = value;
 }
 
-__global__ void copy_f32_kernel(const float* src, float* dst, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (4 * i + 3 < n) {
-    *(f32x4*)(dst + 4 * i) = *(const f32x4*)(src + 4 * i);
-  } else {
-    for (int64_t j = 4 * i; j < n; ++j) dst[j] = src[j];
-  }
-}
 
 hipError_t launch_fill_u8(uint8_t* p, int64_t n, uint8_t value, hipStream_t st) {
   if (n <= 0) return hipSuccess;
@@ -109,12 +101,5 @@ hipError_t launch_fill_f32(float* p, int64_t n, float value, hipStream_t st) {
   return hipGetLastError();
 }
 
-// src and dst 16-byte aligned.
-hipError_t launch_copy_f32(const float* src, float* dst, int64_t n, hipStream_t st) {
-  if (n <= 0) return hipSuccess;
-  const int64_t threads = (n + 3) / 4;
-  hipLaunchKernelGGL(copy_f32_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, src, dst, n);
-  return hipGetLastError();
-}
 
 }  // namespace fb

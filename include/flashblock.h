@@ -300,7 +300,7 @@ typedef struct fb_block_plan {
   float gamma;       /* similarity rule: head h reuses at step s >= 2 when sim_{s-1} > gamma  */
 } fb_block_plan;
 
-/* Workspace bytes for fb_block_run (a step's workspace, a copy of cache_a, similarities). */
+/* Workspace bytes for fb_block_run (a step's workspace, per-row cosine sums, similarities). */
 size_t fb_block_workspace_size(const fb_shape* s);
 
 /* The S steps of one block, each an fb_step, with the reuse mask of every step chosen by
