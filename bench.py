@@ -254,10 +254,31 @@ def cpu_baseline(p):
     per_head = el / (reps * len(heads))
     step_s = per_head * p.h_q
     kv_bytes = p.k.shape[0] * p.h_kv * p.d * 2 * 2
-    return dict(value=kv_bytes / step_s / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
-                sample=f"{len(heads)} of {p.h_q} heads x {reps} reps (full 32768-token prefix + block + merge per "
-                       f"head), scaled to the 32-head step: {step_s * 1e3:.1f} ms per step",
-                step_ms=step_s * 1e3)
+    out = dict(value=kv_bytes / step_s / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
+               sample=f"{len(heads)} of {p.h_q} heads x {reps} reps (full 32768-token prefix + block + merge per "
+                      f"head), scaled to the 32-head step: {step_s * 1e3:.1f} ms per step",
+               step_ms=step_s * 1e3)
+    # one BLAS thread: one head of the same step, scaled to the 32-head step; and the tiny fp32
+    # two-step case (fresh + reuse) whole
+    try:
+        from threadpoolctl import threadpool_limits
+        import synth
+        from oracle.flashblock import step as oracle_step
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            ao, lo = attend(p.q[0, :, 0], p.k[:, 0], p.v[:, 0], p.scale)
+            ai, li = attend(p.q[0, :, 0], p.k_blk[0, :, 0], p.v_blk[0, :, 0], p.scale)
+            lse_merge(ao, lo, ai, li)
+            out["single_thread_step_ms"] = (time.perf_counter() - t0) * p.h_q * 1e3
+            t = synth.tiny()
+            t0 = time.perf_counter()
+            z = np.zeros((1, t.h_q), np.uint8)
+            _, _, ca, cl = oracle_step(t.q, t.k, t.v, t.cu, t.k_blk, t.v_blk, z, None, None, t.scale)
+            oracle_step(t.extra["q_step1"], t.k, t.v, t.cu, t.k_blk, t.v_blk, 1 - z, ca, cl, t.scale)
+            out["single_thread_tiny_two_steps_ms"] = (time.perf_counter() - t0) * 1e3
+    except ImportError:
+        pass
+    return out
 
 
 def main():
