@@ -117,7 +117,7 @@ SplitPlan split_plan(const fb_shape* s, const RowPlan& rp, int64_t max_keys, int
         int64_t best = 1, best_cost = INT64_MAX;
         for (int64_t sp = 1; sp <= 256; ++sp) {
           const int64_t ch = std::max<int64_t>(round_up(cdiv(max_keys, sp), kTileKeys), kMinChunk);
-          if (sp > 1 && cdiv(max_keys, ch) < sp) break;   // more splits than chunks
+          if (cdiv(max_keys, ch) != sp) continue;   // rounding gives another split count: seen or to come
           const int64_t cost = cdiv(fa_items * sp, slots) * (ch + FB_FA_ITEM_OVERHEAD_KEYS);
           if (cost < best_cost) {
             best_cost = cost;
