@@ -9,8 +9,9 @@ pass, chunk reduction, cache write and log-space merge).  The timed step is a fr
 Prints ONE JSON line.  `value` is the K/V bytes of the prefix read per second of step
 time (inputs resident in HBM).  `roofline` is the attention kernel's algorithmic bytes
 over its own average duration (HIP events recorded by the library on its stream around
-that kernel).  `cpu_baseline` is the fp64 oracle timed on the host cores on a bounded
-sample of the same step.  `extra` holds the reuse step, an 8-step block, and the other
+that kernel); beside the published peak it carries the read rate a plain streaming kernel
+reaches on this chip (`measured_peak`, `frac_of_measured`).  `cpu_baseline` is the fp64
+oracle timed on the host cores on a bounded sample of the same step.  `extra` holds the reuse step, an 8-step block, and the other
 workloads (ragged GQA, video block, LoSA sparse step).
 """
 from __future__ import annotations
@@ -338,7 +339,13 @@ def main():
         extra["block8_mean_step_us"] = wall_b / 8 * 1e6
         extra["block8_fresh_steps"] = fresh
         extra["cold_fresh_step_us"] = flushed_step_times(lambda tr: run_step(fb, shape, dev, bufs, m_fresh)) * 1e6
+        ceil = measured_ceilings(kv_bytes)
+        extra["ceilings"] = ceil
         extra["workloads"] = other_workloads(fb, args)
+        vb = extra["workloads"]["video_block"]
+        vb["masked_frac_of_measured_mfma"] = vb["masked_TFLOPs"] / ceil["mfma_bf16_TFLOPs"]
+        vb["attn_kernel_all_fresh_frac_of_measured_mfma"] = (vb["attn_kernel_all_fresh_frac_mfma"] * MFMA_BF16_PEAK_TFLOPS
+                                                            / ceil["mfma_bf16_TFLOPs"])
         extra["context_sweep"] = context_sweep(fb, args)
         extra["lifecycle"] = lifecycle_workload(fb, args)
     result = {
@@ -354,9 +361,55 @@ def main():
                      "kernel": STREAM_KERNEL + " (split-KV prefix + block pass, one launch)"},
         "extra": extra,
     }
+    if "ceilings" in extra:   # the same kernel against the read rate measured on this chip
+        result["roofline"]["measured_peak"] = extra["ceilings"]["stream_read_GBps"]
+        result["roofline"]["frac_of_measured"] = achieved / extra["ceilings"]["stream_read_GBps"]
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(p)
     print(json.dumps(result))
+
+
+def measured_ceilings(nbytes: int):
+    """The rates this chip reaches on the two resources the attention kernels are bound by,
+    measured here beside the published peaks: a streaming read of `nbytes` (one launch at a
+    time, each timed with events, as the attention kernel is) and a register-only bf16 MFMA
+    loop on every CU (2 workgroups of 4 waves per CU, about 2 ms per launch)."""
+    import torch
+    from cached_kv_prefix_amd import ceiling
+    ceiling.load()
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    buf.fill_(0x01010101)
+    wgs = 4096
+    sink = torch.empty((wgs, 4), dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        ceiling.stream_read(buf, nbytes, wgs, sink)
+    times = []
+    for _ in range(20):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ceiling.stream_read(buf, nbytes, wgs, sink)
+        e1.record()
+        times.append((e0, e1))
+    torch.cuda.synchronize()
+    read_s = float(np.mean([a.elapsed_time(b) for a, b in times])) * 1e-3
+    del buf, sink
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    mwg, iters = 2 * n_cu, 16384
+    msink = torch.empty(mwg * 4, device="cuda")
+    ceiling.mfma_loop(mwg, 256, 1.0, 1.0, msink)
+    rates = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ceiling.mfma_loop(mwg, iters, 1.0, 1.0, msink)
+        e1.record()
+        torch.cuda.synchronize()
+        rates.append(ceiling.mfma_flops(mwg, iters) / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    assert (msink.cpu().numpy() == np.float32(64 * iters)).all(), "MFMA loop result"
+    return {"stream_read_GBps": nbytes / read_s / 1e9, "stream_read_us": read_s * 1e6, "stream_read_bytes": nbytes,
+            "mfma_bf16_TFLOPs": float(np.median(rates)), "mfma_workgroups": mwg,
+            "probe": "libfb_ceiling.so: grid-stride 16-byte reads (4096 x 256 threads); "
+                     "4 independent v_mfma_f32_32x32x16_bf16 chains per wave"}
 
 
 def context_sweep(fb, args, lengths=(102400, 204800, 409600, 819200)):

@@ -1,0 +1,59 @@
+/*
+ * fb_ceiling.h — measured ceilings of the GPU the attention library runs on.
+ *
+ * Two plain kernels, in a library of their own (libfb_ceiling.so), that measure what this
+ * chip reaches on the two resources the attention kernels are bound by.  A measurement
+ * helper: no attention work runs here.
+ *   - a streaming read of a device buffer (the HBM read rate a kernel can reach), for the
+ *     prefix pass, whose roofline is HBM (the cached K/V is read once per fresh step:
+ *     "Resumo Técnico: FlashBlock", §2 Mecanismo Central);
+ *   - a loop of independent bf16 matrix FMAs (v_mfma_f32_32x32x16_bf16) with no memory
+ *     traffic, for the long-block pass whose roofline is the matrix units.
+ * Both run under the same power and clock limits as the attention kernels, so their rates
+ * sit beside the published peaks (8 TB/s HBM, 2.5 PFLOP/s dense bf16) as the achievable
+ * ones.  Each writes a result the caller can check exactly, so a reported rate comes from
+ * work that was really done.
+ *
+ * Conventions: the caller allocates every buffer in device memory; the library allocates
+ * nothing and keeps no state.  Work is enqueued on `stream`; nothing synchronises the host.
+ * Arguments are checked on the host before any launch: an invalid argument returns 1 and
+ * launches nothing, a failed launch returns 5, success returns 0 (the numbering of
+ * fb_status in flashblock.h).
+ */
+#ifndef FB_CEILING_H
+#define FB_CEILING_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Read `bytes` bytes of `buf` once, 16 bytes per load, with `workgroups` workgroups of 256
+ * threads striding over the buffer.  Workgroup w writes to sink[16 w .. 16 w + 15] the
+ * bitwise XOR of the 16-byte words it read, so the XOR of all `workgroups` sink entries is
+ * the XOR of every 16-byte word of the buffer.
+ *   buf        device, 16-byte aligned, `bytes` bytes (bytes > 0, bytes % 16 == 0)
+ *   workgroups 1 .. 65536
+ *   sink       device, 16 * workgroups bytes, written
+ */
+int fbc_stream_read(const void* buf, int64_t bytes, int32_t workgroups, void* sink, hipStream_t stream);
+
+/* Run `iters` rounds of 4 independent v_mfma_f32_32x32x16_bf16 per wave on register
+ * operands: `workgroups` workgroups of 4 waves, every element of A set to bf16(a) and of B
+ * to bf16(b).  Work done: workgroups * 4 * iters * 4 * 32768 flops (2 per multiply-add).
+ * Wave j of workgroup w writes to sink[4 w + j] the sum over its 4 accumulators of one
+ * output element, which is exactly 4 * 16 * iters * bf16(a) * bf16(b) when that value and
+ * every partial sum are exact in fp32 (for a = b = 1: iters <= 262144).
+ *   workgroups 1 .. 65536; iters 1 .. 262144
+ *   sink       device, 4 * workgroups floats, written
+ */
+int fbc_mfma_loop(int32_t workgroups, int64_t iters, float a, float b, float* sink, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FB_CEILING_H */

@@ -237,3 +237,37 @@ def test_grid_size_limits_are_rejected_before_launch():
     ls = fb.make_losa_shape(fb.make_shape(65535, 1024, 1024, 128, 1024, seqlen_k=16), page_size=16, topk=1,
                             n_active=1024, max_pages=1)
     assert fb.losa_workspace_size(ls) == 0
+
+
+def ceiling_header_functions():
+    text = open(os.path.join(ROOT, "include", "fb_ceiling.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fbc_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_ceiling_library_exports_every_declared_function():
+    from cached_kv_prefix_amd import ceiling
+    lib = ceiling.load()
+    names = ceiling_header_functions()
+    assert names == sorted(ceiling.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_ceiling_argument_checks_launch_nothing():
+    """Invalid arguments return 1 before any launch (so these run without a GPU)."""
+    from cached_kv_prefix_amd import ceiling
+    lib = ceiling.load()
+    buf, sink = C.c_void_p(0x10000), C.c_void_p(0x20000)
+    assert lib.fbc_stream_read(None, 1024, 4, sink, None) == 1
+    assert lib.fbc_stream_read(buf, 1024, 4, None, None) == 1
+    assert lib.fbc_stream_read(buf, 0, 4, sink, None) == 1
+    assert lib.fbc_stream_read(buf, 1000, 4, sink, None) == 1          # not a multiple of 16 bytes
+    assert lib.fbc_stream_read(buf, 1024, 0, sink, None) == 1
+    assert lib.fbc_stream_read(buf, 1024, 65537, sink, None) == 1
+    assert lib.fbc_stream_read(C.c_void_p(0x10008), 1024, 4, sink, None) == 1   # misaligned
+    assert lib.fbc_mfma_loop(4, 10, 1.0, 1.0, None, None) == 1
+    assert lib.fbc_mfma_loop(0, 10, 1.0, 1.0, sink, None) == 1
+    assert lib.fbc_mfma_loop(65537, 10, 1.0, 1.0, sink, None) == 1
+    assert lib.fbc_mfma_loop(4, 0, 1.0, 1.0, sink, None) == 1
+    assert lib.fbc_mfma_loop(4, 262145, 1.0, 1.0, sink, None) == 1

@@ -1,0 +1,40 @@
+"""The measured-ceiling kernels (include/fb_ceiling.h) on the GPU: the streaming read
+touches every 16-byte word of its buffer exactly once (the XOR of the workgroups' sink
+entries equals the XOR of the buffer, computed on the host), and the MFMA loop does all the
+multiply-adds it is counted for (its per-wave sums are exact)."""
+import numpy as np
+import pytest
+
+from tests.gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("nbytes,workgroups", [(16, 1), (4096, 3), (1_000_000 * 16, 7), (536_870_912, 4096),
+                                                (536_870_912 + 48, 1024)])
+def test_stream_read_reads_every_word_once(gpu_lib, nbytes, workgroups):
+    import torch
+    from cached_kv_prefix_amd import ceiling
+    say(f"[ceiling] stream read {nbytes} B, {workgroups} workgroups")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(nbytes % 1000003)
+    words = torch.randint(-(1 << 31), (1 << 31) - 1, (nbytes // 4,), dtype=torch.int32, device="cuda", generator=g)
+    sink = torch.full((workgroups, 4), -1, dtype=torch.int32, device="cuda")
+    ceiling.stream_read(words, nbytes, workgroups, sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32), axis=0)
+    want = np.bitwise_xor.reduce(words.cpu().numpy().view(np.uint32).reshape(-1, 4), axis=0)
+    assert (got == want).all(), (got, want)
+
+
+@pytest.mark.parametrize("workgroups,iters,a,b", [(1, 1, 1.0, 1.0), (5, 1000, 1.0, 1.0), (512, 262144, 1.0, 1.0),
+                                                  (256, 4096, 0.5, -2.0)])
+def test_mfma_loop_does_the_counted_work(gpu_lib, workgroups, iters, a, b):
+    import torch
+    from cached_kv_prefix_amd import ceiling
+    say(f"[ceiling] mfma loop {workgroups} workgroups x {iters} iterations")
+    sink = torch.full((workgroups * 4,), float("nan"), device="cuda")
+    ceiling.mfma_loop(workgroups, iters, a, b, sink)
+    torch.cuda.synchronize()
+    want = 4 * 16 * iters * a * b
+    assert (sink.cpu().numpy() == np.float32(want)).all(), sink[:8]
