@@ -104,11 +104,26 @@ __global__ void sim_reduce_kernel(int batch, int B, int h_q, const double* parts
   if (bh >= (int64_t)batch * h_q) return;
   const int h = bh % h_q, b = bh / h_q;
   double xy = 0.0, xx = 0.0, yy = 0.0;
-  for (int i = 0; i < B; ++i) {
-    const double* p = parts + (((int64_t)b * B + i) * h_q + h) * 3;
-    xy += p[0];
-    xx += p[1];
-    yy += p[2];
+  const double* base = parts + ((int64_t)b * B * h_q + h) * 3;
+  const int64_t step = (int64_t)h_q * 3;
+  int i = 0;
+  for (; i + 8 <= B; i += 8) {   // eight rows' loads in flight, then added in row order
+    double v[8][3];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int c = 0; c < 3; ++c) v[u][c] = base[(i + u) * step + c];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      xy += v[u][0];
+      xx += v[u][1];
+      yy += v[u][2];
+    }
+  }
+  for (; i < B; ++i) {
+    xy += base[i * step + 0];
+    xx += base[i * step + 1];
+    yy += base[i * step + 2];
   }
   const float s = (xx == 0.0 || yy == 0.0) ? 0.f : (float)(xy / (sqrt(xx) * sqrt(yy)));
   sim[bh] = s;
