@@ -911,6 +911,7 @@ fb_status fb_prefix_attn_varlen(const fb_varlen_shape* vs, const void* q, const 
   a.B = 0;   // queries are addressed by the packed row map alone
   a.src0 = make_src(p.step.rp, p.step.pre, k, v, s->cu_seqlens_k, s->seqlen_k, (float*)ws, p.step.rpre);
   a.src0.row_tok = row_tok;
+  a.src0.cu_q = vs->cu_seqlens_q;
   if (hipError_t e = launch_attn(a, s->dtype == FB_BF16, stream)) return hip_status(e);
   CombineArgs c = base_combine(s, p.step, (float*)ws);
   c.mode = kModePrefixOnly;

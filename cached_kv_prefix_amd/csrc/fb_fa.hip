@@ -54,12 +54,13 @@ __device__ __forceinline__ int fa_qtiles(const AttnSrc& S, int rows_per_wg) {
   return (S.rows + rows_per_wg - 1) / rows_per_wg;
 }
 
-template <int QT, int W, bool DEEP, bool PAGED>
+template <int QT, int W, bool DEEP, bool PAGED, bool PACKED>
 __global__ void __launch_bounds__(64 * W, QT == 1 && W == 4 ? 2 : 1) attn_fa_kernel(const AttnArgs A) {
   constexpr int D = 128;
   constexpr int ROWS_WG = 32 * W * QT;
   constexpr int NP = 16 / W;                    // 16-byte pieces per thread per K (or V) tile
   static_assert(!PAGED || DEEP, "paged sources run on the deep-prefetch variant");
+  static_assert(!PACKED || (DEEP && !PAGED), "packed queries run on the contiguous deep-prefetch variant");
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][2 * kFaTileBytes];   // [buf][K | V]
   __shared__ int32_t pl_lds[PAGED ? kFaMaxChunkPages : 1];                         // the chunk's pages
 
@@ -113,6 +114,20 @@ __global__ void __launch_bounds__(64 * W, QT == 1 && W == 4 ? 2 : 1) attn_fa_ker
 #pragma unroll
       for (int i2 = 0; i2 < D / 16; ++i2) qf[qi][i2] = bf16x8{};
     }
+  }
+
+  // Packed queries: a wave whose rows are all padding (row i >= the branch's query count)
+  // takes its share of the K / V tile loads and barriers but computes and writes nothing.
+  bool wave_on = true;
+  if constexpr (PACKED) {
+    const int nb = S.cu_q[b + 1] - S.cu_q[b];
+    bool lane_on = false;
+#pragma unroll
+    for (int qi = 0; qi < QT; ++qi) {
+      const int row = r0 + w * 32 * QT + 32 * qi + ql;
+      lane_on |= row < rows && row % S.rows_per_head < nb;
+    }
+    wave_on = __builtin_amdgcn_readfirstlane((int)(__ballot(lane_on) != 0)) != 0;
   }
 
   // ---- K / V tiles: thread piece u = row (tid >> 4) + 16 u, 16-byte chunk tid & 15 ------
@@ -280,6 +295,7 @@ __global__ void __launch_bounds__(64 * W, QT == 1 && W == 4 ? 2 : 1) attn_fa_ker
       const int key_ = kbeg + (T) * kFaTile + lane;                                              \
       vm_ = __ballot(key_ < kend && (unsigned)paged_tok(key_) < (unsigned)si.n_seq);             \
     }                                                                                            \
+    if (!PACKED || wave_on) {                                                                    \
     FA_QK(acc, lds[CUR]);                                                                        \
     if (PAGED && vm_ != ~0ull) {   /* register r of half s holds key 32 s + 8 (r >> 2) + 4 g + (r & 3) */ \
       _Pragma("unroll") for (int s = 0; s < 2; ++s) {                                            \
@@ -299,6 +315,7 @@ __global__ void __launch_bounds__(64 * W, QT == 1 && W == 4 ? 2 : 1) attn_fa_ker
     }                                                                                            \
     FA_SOFTMAX(acc, pb);                                                                         \
     FA_PV(pb, lds[CUR] + kFaTileBytes);                                                          \
+    }                                                                                            \
     FA_STORE_K((CUR) ^ 1, (CUR) ^ 1);                                                            \
     FA_STORE_V((CUR) ^ 1, (CUR) ^ 1);                                                            \
     __syncthreads();                                                                             \
@@ -390,7 +407,7 @@ __global__ void __launch_bounds__(64 * W, QT == 1 && W == 4 ? 2 : 1) attn_fa_ker
 #pragma unroll
   for (int qi = 0; qi < QT; ++qi) {
     const int row = r0 + w * 32 * QT + 32 * qi + ql;
-    if (row >= rows) continue;
+    if (row >= rows || (PACKED && !wave_on)) continue;
 #pragma unroll
     for (int d4 = 0; d4 < D / 32; ++d4)
 #pragma unroll
@@ -439,12 +456,16 @@ hipError_t launch_fa(const AttnArgs& a, hipStream_t st) {
     return hipErrorInvalidValue;
   if (paged && fa_waves(rows) != 4) return hipErrorInvalidValue;
   // up to 128 rows the pass streams K / V (deep prefetch); larger groups are matrix bound
+  // packed queries (one source, no pages): waves of padding rows skip their compute
+  const bool packed = a.src0.cu_q != nullptr && a.src1.n_splits == 0 && !paged;
   if (paged)
-    hipLaunchKernelGGL((attn_fa_kernel<kFaQt, 4, true, true>), dim3((unsigned)n), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_fa_kernel<kFaQt, 4, true, true, false>), dim3((unsigned)n), dim3(256), 0, st, a);
+  else if (fa_waves(rows) == 4 && packed)
+    hipLaunchKernelGGL((attn_fa_kernel<kFaQt, 4, true, false, true>), dim3((unsigned)n), dim3(256), 0, st, a);
   else if (fa_waves(rows) == 4)
-    hipLaunchKernelGGL((attn_fa_kernel<kFaQt, 4, true, false>), dim3((unsigned)n), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_fa_kernel<kFaQt, 4, true, false, false>), dim3((unsigned)n), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_fa_kernel<kFaQt, 8, false, false>), dim3((unsigned)n), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((attn_fa_kernel<kFaQt, 8, false, false, false>), dim3((unsigned)n), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 

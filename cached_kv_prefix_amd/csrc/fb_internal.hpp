@@ -25,6 +25,7 @@ struct AttnSrc {
   int32_t n_splits;           // grid extent along x for this source
   int32_t rows_per_head;
   const int32_t* row_tok;     // [batch][rows_per_head] or null
+  const int32_t* cu_q;        // packed queries: rows i >= cu_q[b+1] - cu_q[b] are padding, or null
   int32_t rows;               // G * rows_per_head
   int32_t tq;                 // 32-row query tiles per workgroup (1, 2 or 4)
   int32_t qgroups;            // ceil(rows / (32 * tq))
