@@ -598,7 +598,8 @@ def other_workloads(fb, args):
         fb.losa_step(ls, qc, qp, dev["k"], dev["v"], dev["k_blk"], dev["v_blk"], kmin, kmax, bufs["ca"], bufs["cl"],
                      bufs["af"], bufs["lf"], sel["active"], sel["topk"], sel["union"], sel["count"], sel["ws"],
                      trace=tr)
-    w_s, a_s, _ = time_steps(sparse, steps, 2)
+    # a short step (about 0.1 ms): the full step count and more warm-up, as for the dLLM steps
+    w_s, a_s, _ = time_steps(sparse, args.steps, 5)
     cnt = sel["count"].cpu().numpy()
     union_bytes = float(cnt.sum()) * 16 * p.d * 2 * 2
     meta_bytes = 2 * fb.losa_meta_bytes(ls)
@@ -606,13 +607,13 @@ def other_workloads(fb, args):
                           "union_pages_mean": float(cnt.mean()), "density": float(cnt.mean()) / ls.max_pages,
                           "alg_bytes": meta_bytes + union_bytes,
                           "frac_hbm_step": (meta_bytes + union_bytes) / w_s / 1e9 / HBM_PEAK_GBS}
-    out["sparse_residual"] = residual_workload(fb, p, dev, shape, sel, cap, steps)
+    out["sparse_residual"] = residual_workload(fb, p, dev, shape, sel, cap, steps, args.steps)
     del dev, bufs, kmin, kmax
     out["multi_branch_varlen"] = varlen_workload(fb, args)
     return out
 
 
-def residual_workload(fb, p, dev, shape, sel, cap, steps):
+def residual_workload(fb, p, dev, shape, sel, cap, steps, short_steps):
     """FlashBlock with a cached sparse residual on the LoSA workload's shape: the selection
     is the union the LoSA selection just produced (per KV head, about 500 of 8192 pages).
     A refresh step attends to the selection and to its complement (the whole prefix) and
@@ -631,9 +632,9 @@ def residual_workload(fb, p, dev, shape, sel, cap, steps):
                                            sel["count"], mask, bufs["ca"], bufs["cl"], bufs["af"], bufs["lf"],
                                            bufs["ws"], trace=tr)
     w_f, a_f, _ = time_steps(step(None), steps, 2)
-    w_r, a_r, _ = time_steps(step(ones), steps, 2)
+    w_r, a_r, _ = time_steps(step(ones), short_steps, 5)   # a short step: more calls, more warm-up
     g_f = graph_step_time(step(None), steps)
-    g_r = graph_step_time(step(ones), steps)
+    g_r = graph_step_time(step(ones), short_steps)
     cnt = sel["count"].cpu().numpy()
     sel_bytes = float(np.minimum(cnt * 16, p.seqlens[0]).sum()) * d * 2 * 2
     all_bytes = float(p.seqlens[0]) * p.h_kv * d * 2 * 2

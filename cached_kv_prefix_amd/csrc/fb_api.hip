@@ -464,7 +464,7 @@ fb_status run_selection(const losa_shape* ls, const LosaPlan& p, const void* q_c
   double* scores = (double*)((char*)ws + p.scores_off);
   double* loc = (double*)((char*)ws + p.loc_off);
   if (hipError_t e = launch_locality(la, q_cur, q_prev, loc, active, stream)) return hip_status(e);
-  if (hipError_t e = launch_quest_scores(la, q_cur, active, kmin, kmax, scores, stream)) return hip_status(e);
+  if (hipError_t e = launch_quest_scores(la, q_cur, loc, active, kmin, kmax, scores, stream)) return hip_status(e);
   if (hipError_t e = launch_topk(la, scores, topk_pages, stream)) return hip_status(e);
   return hip_status(launch_union(la, topk_pages, union_pages, union_count, stream));
 }

@@ -128,7 +128,9 @@ hipError_t launch_page_meta(const LosaArgs& a, const void* k, void* kmin, void* 
                             hipStream_t st);
 hipError_t launch_locality(const LosaArgs& a, const void* qc, const void* qp, double* loc,
                            int32_t* active, hipStream_t st);
-hipError_t launch_quest_scores(const LosaArgs& a, const void* qc, const int32_t* active,
+// The active set is ranked by launch_locality (blocks of more than 256 tokens) or inside
+// launch_quest_scores from the locality scores `loc` (which then writes `active`).
+hipError_t launch_quest_scores(const LosaArgs& a, const void* qc, const double* loc, int32_t* active,
                                const void* kmin, const void* kmax, double* scores,
                                hipStream_t st);
 hipError_t launch_topk(const LosaArgs& a, const double* scores, int32_t* topk_pages,

@@ -140,12 +140,34 @@ __global__ void __launch_bounds__(64) locality_kernel(const LosaArgs a, const vo
   }
 }
 
-// Locality score, part 2: the active set of each sequence, the n_active largest scores
-// (ties to the lower token), listed ascending.
-__global__ void __launch_bounds__(256) active_kernel(const LosaArgs a, const double* loc, int32_t* active) {
-  __shared__ double sc[1024];
-  __shared__ int sel[1024];
-  const int b = blockIdx.x, B = a.B;
+// Locality score, part 2: the active set of sequence b, the n_active largest scores (ties
+// to the lower token), listed ascending.  A workgroup of 256 threads ranks every score
+// against all B of them; sc and sel are LDS arrays of at least B entries.  The list goes to
+// act_lds (LDS, when set) and to active (global, when set).  Ends with a barrier.
+__device__ __forceinline__ void rank_active(const LosaArgs& a, const double* loc, int b, double* sc, int* sel,
+                                            int* act_lds, int32_t* active) {
+  const int B = a.B;
+  if (B <= 64) {   // one score per lane; every wave ranks them alike and wave 0 writes the list
+    const int lane = threadIdx.x & 63;
+    const double si = lane < B ? loc[(int64_t)b * B + lane] : 0.0;
+    const int64_t bits = __builtin_bit_cast(int64_t, si);
+    int rank = 0;
+    for (int j = 0; j < B; ++j) {
+      const int lo = __builtin_amdgcn_readlane((int)(uint32_t)bits, j);
+      const int hi = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)bits >> 32), j);
+      const double sj = __builtin_bit_cast(double, ((int64_t)hi << 32) | (uint32_t)lo);
+      rank += (sj > si || (sj == si && j < lane)) ? 1 : 0;
+    }
+    const bool take = lane < B && rank < a.n_active;
+    const uint64_t m = __ballot(take);
+    const int pos = __popcll(m & ((1ull << lane) - 1));
+    if (take && threadIdx.x < 64) {
+      if (act_lds) act_lds[pos] = lane;
+      if (active) active[b * a.n_active + pos] = lane;
+    }
+    __syncthreads();
+    return;
+  }
   for (int i = threadIdx.x; i < B; i += 256) sc[i] = loc[(int64_t)b * B + i];
   __syncthreads();
   for (int i = threadIdx.x; i < B; i += 256) {
@@ -162,8 +184,17 @@ __global__ void __launch_bounds__(256) active_kernel(const LosaArgs a, const dou
     if (!sel[i]) continue;
     int pos = 0;
     for (int j = 0; j < i; ++j) pos += sel[j];
-    active[b * a.n_active + pos] = i;
+    if (act_lds) act_lds[pos] = i;
+    if (active) active[b * a.n_active + pos] = i;
   }
+  __syncthreads();
+}
+
+// Blocks of more than kRankInQuest tokens: the active sets in a launch of their own.
+__global__ void __launch_bounds__(256) active_kernel(const LosaArgs a, const double* loc, int32_t* active) {
+  __shared__ double sc[1024];
+  __shared__ int sel[1024];
+  rank_active(a, loc, blockIdx.x, sc, sel, nullptr, active);
 }
 
 // QUEST page scores.  grid (page blocks of 128 * kQpp, h_kv, batch), 256 threads.  Lane l
@@ -175,11 +206,18 @@ __global__ void __launch_bounds__(256) active_kernel(const LosaArgs a, const dou
 // exactly: one of the two products is zero, the other is exact in fp64 and rounds once, as
 // in the left-to-right fp64 sum over d of the definition.
 constexpr int kQpp = 4;
+constexpr int kRankInQuest = 256;   // blocks up to this size rank their active set inside the QUEST launch
 constexpr int kQRow = 257;   // LDS row stride (pairs): the two half-waves' rows fall in different banks
 template <bool BF16>
-__global__ void __launch_bounds__(256) quest_score_kernel(const LosaArgs a, const void* qc, const int32_t* active,
-                                                          const void* kmin, const void* kmax, double* scores) {
+// With loc set (blocks of at most kRankInQuest tokens), every workgroup ranks its
+// sequence's locality scores itself, and workgroup (0, 0, b) writes the active list, which
+// the later launches of the step read; otherwise `active` holds the list already.
+__global__ void __launch_bounds__(256) quest_score_kernel(const LosaArgs a, const void* qc, const double* loc,
+                                                          int32_t* active, const void* kmin, const void* kmax,
+                                                          double* scores) {
   __shared__ __attribute__((aligned(16))) double qpn[8][kQRow][2];
+  __shared__ double rank_sc[kRankInQuest];
+  __shared__ int rank_sel[kRankInQuest], act_lds[kRankInQuest];
   const int b = blockIdx.z, hk = blockIdx.y;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, rg = lane >> 5;
   const int p0 = ((blockIdx.x * 4 + w) * 32 + (lane & 31)) * kQpp;
@@ -206,6 +244,18 @@ __global__ void __launch_bounds__(256) quest_score_kernel(const LosaArgs a, cons
     else
       return (double)x[e];
   };
+  // The first chunk's metadata does not depend on the rows: it is in flight while the
+  // active set is ranked and the first rows of q are staged.
+  Raw mn[kQpp], mx[kQpp];
+  auto load_first = [&]() {
+#pragma unroll
+    for (int u = 0; u < kQpp; ++u) {
+      mn[u] = load_meta(kmin, 0, u);
+      mx[u] = load_meta(kmax, 0, u);
+    }
+  };
+  if (p0 < P) load_first();
+  if (loc) rank_active(a, loc, b, rank_sc, rank_sel, act_lds, blockIdx.x == 0 && blockIdx.y == 0 ? active : nullptr);
   for (int r0 = 0; r0 < R; r0 += 8) {
     const int nr = min(8, R - r0);
     __syncthreads();
@@ -215,7 +265,7 @@ __global__ void __launch_bounds__(256) quest_score_kernel(const LosaArgs a, cons
       if (rr < nr) {
         const int r = r0 + rr;
         const int h = hk * a.G + r / a.n_active;
-        const int tok = active[b * a.n_active + r % a.n_active];
+        const int tok = loc ? act_lds[r % a.n_active] : active[b * a.n_active + r % a.n_active];
         q = load_elem(qc, (((int64_t)b * a.B + tok) * a.h_q + h) * d + j, a.bf16);
       }
       qpn[rr][j][0] = q > 0.0 ? q : 0.0;
@@ -228,12 +278,7 @@ __global__ void __launch_bounds__(256) quest_score_kernel(const LosaArgs a, cons
     for (int u = 0; u < kQpp; ++u)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) acc[u][rr] = 0.0;
-    Raw mn[kQpp], mx[kQpp];
-#pragma unroll
-    for (int u = 0; u < kQpp; ++u) {
-      mn[u] = load_meta(kmin, 0, u);
-      mx[u] = load_meta(kmax, 0, u);
-    }
+    if (r0 > 0) load_first();
     for (int c = 0; c < nc; ++c) {
       Raw cn[kQpp], cx[kQpp];
 #pragma unroll
@@ -488,17 +533,21 @@ hipError_t launch_locality(const LosaArgs& a, const void* qc, const void* qp, do
                            hipStream_t st) {
   hipLaunchKernelGGL(locality_kernel, dim3(a.B, a.batch), dim3(64), 0, st, a, qc, qp, loc);
   if (hipError_t e = hipGetLastError()) return e;
+  if (a.B <= kRankInQuest) return hipSuccess;   // ranked inside the QUEST launch
   hipLaunchKernelGGL(active_kernel, dim3(a.batch), dim3(256), 0, st, a, loc, active);
   return hipGetLastError();
 }
 
-hipError_t launch_quest_scores(const LosaArgs& a, const void* qc, const int32_t* active, const void* kmin,
-                               const void* kmax, double* scores, hipStream_t st) {
+hipError_t launch_quest_scores(const LosaArgs& a, const void* qc, const double* loc, int32_t* active,
+                               const void* kmin, const void* kmax, double* scores, hipStream_t st) {
   dim3 grid((unsigned)((a.max_pages + 128 * kQpp - 1) / (128 * kQpp)), a.h_kv, a.batch);
+  const double* rank_loc = a.B <= kRankInQuest ? loc : nullptr;
   if (a.bf16)
-    hipLaunchKernelGGL(quest_score_kernel<true>, grid, dim3(256), 0, st, a, qc, active, kmin, kmax, scores);
+    hipLaunchKernelGGL(quest_score_kernel<true>, grid, dim3(256), 0, st, a, qc, rank_loc, active, kmin, kmax,
+                       scores);
   else
-    hipLaunchKernelGGL(quest_score_kernel<false>, grid, dim3(256), 0, st, a, qc, active, kmin, kmax, scores);
+    hipLaunchKernelGGL(quest_score_kernel<false>, grid, dim3(256), 0, st, a, qc, rank_loc, active, kmin, kmax,
+                       scores);
   return hipGetLastError();
 }
 

@@ -65,6 +65,10 @@ SMALL = [
     ("few_pages", 1, 2, 1, 64, 8, [40], 2, 16, 8, "bf16"),
     ("page1", 1, 2, 2, 64, 8, [70], 2, 1, 9, "bf16"),
     ("f32", 1, 2, 1, 64, 8, [300], 3, 16, 4, "f32"),
+    # the active set is ranked inside the page-score launch up to 256 block tokens, in a
+    # launch of its own above that
+    ("block256_rank_in_quest", 1, 2, 2, 64, 256, [400], 7, 16, 5, "bf16"),
+    ("block300_rank_own_launch", 1, 2, 2, 64, 300, [500], 5, 16, 6, "bf16"),
 ]
 
 
@@ -137,6 +141,24 @@ def test_topk_ties_go_to_lower_pages(gpu_lib):
     exp = OL.select_union(q_cur, q_prev, p.k, p.cu, 2, 3, 16, 6)
     _check_selection(p, out, exp, 3)
     assert np_of(out["topk"]).max() < 40
+
+
+@pytest.mark.parametrize("B", [16, 300])
+def test_active_set_ties_go_to_lower_tokens(gpu_lib, B):
+    """Unchanged queries give every block token the locality score 0: the active set is
+    then the lowest tokens, on both ranking paths (inside the page-score launch, and in a
+    launch of its own for blocks of more than 256 tokens)."""
+    import torch
+    fb = gpu_lib
+    say(f"[losa] ranking ties, B {B}")
+    p = synth.custom(7, 1, 2, 2, 64, B, [200], std=1.0)
+    dev, s, ls, out = _setup(fb, p, p.q, p.q, 5, 16, 4)
+    fb.losa_select_union(ls, dev["q_cur"], dev["q_prev"], dev["kmin"], dev["kmax"], out["active"], out["topk"],
+                         out["union"], out["count"], out["ws"])
+    torch.cuda.synchronize()
+    exp = OL.select_union(p.q, p.q, p.k, p.cu, 2, 5, 16, 4)
+    assert (exp["active"] == np.arange(5)).all()
+    _check_selection(p, out, exp, 5)
 
 
 def test_losa_full_size(gpu_lib):
