@@ -36,6 +36,9 @@ CASES = [
     ("stream_blocks_4_to_32", [4, 8, 16, 32], [300, 517, 93, 1000], 4, 4, 128, 32, "bf16"),
     ("tiled_blocks_to_128", [4, 128, 64, 0, 33], [700, 2000, 0, 50, 129], 2, 2, 128, 128, "bf16"),
     ("gqa4_stream", [8, 2, 5], [640, 1280, 77], 8, 2, 128, 8, "bf16"),
+    # 2 query heads x 48 rows: a wave's 32 rows straddle the two heads, so a wave is idle
+    # only where both heads' rows are padding (branch of 10: waves 0 and 1 work, 2 is idle)
+    ("gqa2_tiled_heads_straddle", [40, 10, 48, 17], [500, 900, 300, 64], 4, 2, 128, 48, "bf16"),
     ("wide_256", [256, 100, 3], [900, 400, 1500], 1, 1, 128, 256, "bf16"),
     ("d64", [4, 16, 9], [200, 333, 64], 4, 2, 64, 16, "bf16"),
     ("f32", [3, 8, 1], [100, 40, 77], 4, 2, 32, 8, "f32"),
