@@ -26,6 +26,10 @@
 //     LDS once; each load piece computes its token offset without branches, and a key
 //     past the chunk or a token outside the sequence gets an out-of-range offset (reads
 //     zero) and is masked by the tile's validity ballot;
+//   * packed queries (PACKED, DEEP only: the multi-branch pass, every branch padded to the
+//     longest block): a wave whose rows are all padding of its branch loads its share of
+//     each tile and meets every barrier but runs no matrix or softmax work and writes no
+//     partial, so short branches cost memory time only;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K rows chunk-swizzled by key & 15 for
 //     conflict-free ds_read_b128); softmax in registers, one query per lane; O^T = V^T P^T
 //     with V^T from ds_read_b64_tr_b16 (V rows swizzled by key & 3);
