@@ -7,8 +7,10 @@
 // The page score is the maximum of q.k over the page's per-dimension key box,
 //   S = sum_d max(q_d kmin_d, q_d kmax_d) = sum_d q_d * (q_d >= 0 ? kmax_d : kmin_d).
 // Every decision is taken in fp64 with sums in a fixed left-to-right order (per head
-// over dims, then over heads, for the locality score; over dims for the page score) and
-// without fused multiply-add, so the selected indices are exactly reproducible.
+// over dims, then over heads, for the locality score; over dims for the page score), and
+// the compiler may not contract a multiply and an add into one rounding, so the selected
+// indices are exactly reproducible.  The page score's explicit two-FMA step is the one
+// exception, and it rounds exactly as the plain sum does (see quest_score_kernel).
 #include "fb_device.hpp"
 #include "fb_internal.hpp"
 #include <type_traits>
