@@ -189,7 +189,7 @@ __global__ void __launch_bounds__(256, FB_ATTN_OCC) attn_bf16_kernel(const AttnA
         sv[r] = fast_exp2(sv[r] - m_use);
         ps += sv[r];
       }
-      ps += __shfl_xor(ps, 32);
+      ps = wave_add_xor32(ps);
       l_run = l_run * alpha + ps;
       m_run = m_new;
 #pragma unroll

@@ -36,8 +36,18 @@ __device__ __forceinline__ float exp2_or_zero(float x) {
   return x == kNegInf ? 0.0f : fast_exp2(x);
 }
 
+// Max / sum of a lane's value with the value of the lane 32 away, through
+// v_permlane32_swap (a VALU lane swap, no LDS round trip).  With x in both operands the
+// two results hold, in every lane l, x[l & 31] and x[(l & 31) + 32]; max and + of two
+// operands are commutative, so every lane gets exactly fmax(x[l], x[l ^ 32]) and
+// x[l] + x[l ^ 32].
 __device__ __forceinline__ float wave_max_xor32(float x) {
-  return fmaxf(x, __shfl_xor(x, 32));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float wave_add_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ float wave_sum(float x) {

@@ -257,7 +257,7 @@ __global__ void __launch_bounds__(64 * W, QT == 1 && W == 4 ? 2 : 1) attn_fa_ker
           ps += p_;                                                                              \
           PB[qi][2 * s + c][jj] = (__bf16)p_;                                                    \
         }                                                                                        \
-    ps += __shfl_xor(ps, 32);                                                                    \
+    ps = wave_add_xor32(ps);                                                                     \
     l_run[qi] += ps;                                                                             \
   }
   // O^T += V^T P^T: k-step (s, c) covers keys 32 s + 16 c + 8 (j >> 2) + 4 g + (j & 3).

@@ -248,7 +248,7 @@ _Pragma("unroll")                                                               
       sv[r] = fast_exp2(fmaf(acc[r], A.scale_log2, -m_use));                                \
       ps += sv[r];                                                                          \
     }                                                                                       \
-    ps += __shfl_xor(ps, 32);                                                               \
+    ps = wave_add_xor32(ps);                                                                \
     l_run += ps;                                                                            \
 _Pragma("unroll")                                                                           \
     for (int c = 0; c < 2; ++c) {                                                           \
