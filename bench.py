@@ -174,10 +174,11 @@ def graph_step_time(fn, steps, warmup=3):
     return wall
 
 
-def flushed_step_times(fn, n=10):
+def flushed_step_times(fn, n=100):
     """Per-step event timing after a 1 GiB read before each step (outside the events), so
     the 256 MB last-level cache holds none of the inputs.  A read, not a write: dirty
-    lines left by a write would be written back during the timed step."""
+    lines left by a write would be written back during the timed step.  Returns the
+    per-step times (s)."""
     import torch
     scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     sink = torch.empty((), dtype=torch.float32, device="cuda")
@@ -191,7 +192,7 @@ def flushed_step_times(fn, n=10):
         torch.cuda.synchronize()
         out.append(a.elapsed_time(b) / 1e3)
     del scratch
-    return float(np.median(out))
+    return out
 
 
 STREAM_KERNEL = "fb::attn_stream_kernel<1, 40, false>"
@@ -338,7 +339,9 @@ def main():
         fresh = int(1 + (p.extra["m_updated"][1:, 0] >= 4).sum())
         extra["block8_mean_step_us"] = wall_b / 8 * 1e6
         extra["block8_fresh_steps"] = fresh
-        extra["cold_fresh_step_us"] = flushed_step_times(lambda tr: run_step(fb, shape, dev, bufs, m_fresh)) * 1e6
+        cold = np.asarray(flushed_step_times(lambda tr: run_step(fb, shape, dev, bufs, m_fresh))) * 1e6
+        extra["cold_fresh_step_us"] = float(np.median(cold))
+        extra["cold_fresh_step_us_p10_p50_p90"] = [float(x) for x in np.percentile(cold, [10, 50, 90])]
         ceil = measured_ceilings(kv_bytes)
         extra["ceilings"] = ceil
         extra["workloads"] = other_workloads(fb, args)
