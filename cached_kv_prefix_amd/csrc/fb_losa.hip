@@ -343,23 +343,120 @@ __device__ __forceinline__ uint64_t wave_or64(uint64_t x) {
   return x;
 }
 
-// One workgroup per (b, h, active row): exact top-k by (score desc, page asc) with an
-// MSB-first radix select (8-bit digits) on order-preserving 64-bit keys.  Thread t holds
-// the keys of pages t + 256 j in registers (coalesced loads).  Leading bytes common to all
-// keys are skipped; each remaining pass builds a 256-bucket histogram of the keys that
-// match the prefix so far, and a block scan over the buckets (highest digit first) picks
-// the digit of the k-th largest key.  The selection is then two LDS bitmaps (keys above
-// it, keys equal to it; one ballot per wave and j gives one 64-page word): equal keys are
-// taken lowest pages first, and the result is compacted in ascending page order.  Fewer
-// than k pages: all of them, padded with -1.
+// Exact top-k by (score desc, page asc) with an MSB-first radix select (8-bit digits) on
+// order-preserving 64-bit keys.  Thread t holds keys t + 256 j, j < N, of which those below
+// `limit` are real (at least K of them).
+// Leading bytes common to all keys are skipped; each remaining pass builds a 256-bucket
+// histogram of the keys that match the prefix so far, and a block scan over the buckets
+// (highest digit first) picks the digit of the k-th largest key.  The passes stop as soon
+// as the bucket holding it is exactly what is still needed.  On return: the selected keys
+// are those with (key & pmask) > prefix, plus `need` of those with (key & pmask) == prefix
+// (lowest pages first).
+struct TopkShared {
+  int hist[256];
+  int tmp[4];
+  int digit, above, count;
+  unsigned long long kand, kor;
+};
+
+template <int N>
+__device__ __forceinline__ void radix_select(const uint64_t (&key)[N], int limit, int K, TopkShared& sh,
+                                             uint64_t& prefix_out, uint64_t& pmask_out, int& need_out) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid == 0) {
+    sh.kand = ~0ull;
+    sh.kor = 0ull;
+  }
+  __syncthreads();
+  {
+    uint64_t ka = ~0ull, ko = 0ull;
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+      if (tid + 256 * j < limit) {
+        ka &= key[j];
+        ko |= key[j];
+      }
+    ka = wave_and64(ka);
+    ko = wave_or64(ko);
+    if (lane == 0) {
+      atomicAnd(&sh.kand, (unsigned long long)ka);
+      atomicOr(&sh.kor, (unsigned long long)ko);
+    }
+  }
+  __syncthreads();
+  const uint64_t diff = sh.kand ^ sh.kor;
+  int pass0 = 0;
+  while (pass0 < 8 && ((diff >> (56 - 8 * pass0)) & 255) == 0) ++pass0;
+  uint64_t pmask = pass0 == 0 ? 0ull : (pass0 == 8 ? ~0ull : ~0ull << (64 - 8 * pass0));
+  uint64_t prefix = sh.kand & pmask;
+  int need = K;
+  for (int pass = pass0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    sh.hist[tid] = 0;
+    __syncthreads();
+    // when every matching lane of a wave has the same digit (common in the leading
+    // passes) the wave adds its count with one atomic
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const bool match = tid + 256 * j < limit && (key[j] & pmask) == prefix;
+      const int dg = (int)((key[j] >> shift) & 255);
+      const uint64_t m = __ballot(match);
+      if (m) {
+        const int leader = __ffsll((unsigned long long)m) - 1;
+        const int ldg = __builtin_amdgcn_readlane(dg, leader);
+        if (__ballot(match && dg == ldg) == m) {
+          if (lane == leader) atomicAdd(&sh.hist[ldg], (int)__popcll(m));
+        } else if (match) {
+          atomicAdd(&sh.hist[dg], 1);
+        }
+      }
+    }
+    __syncthreads();
+    // thread t looks at digit 255 - t: inclusive count of keys with a digit >= 255 - t
+    const int c = sh.hist[255 - tid];
+    int total;
+    const int cum = block_incl_scan(c, sh.tmp, &total);
+    if (cum >= need && cum - c < need) {
+      sh.digit = 255 - tid;
+      sh.above = cum - c;
+      sh.count = c;
+    }
+    __syncthreads();
+    need -= sh.above;
+    prefix |= (uint64_t)sh.digit << shift;
+    pmask |= (uint64_t)255 << shift;
+    const bool whole = sh.count == need;          // the bucket is exactly what is still needed
+    __syncthreads();
+    if (whole) break;
+  }
+  prefix_out = prefix;
+  pmask_out = pmask;
+  need_out = need;
+}
+
+// One workgroup per (b, h, active row).  Thread t holds the keys of pages t + 256 j in
+// registers (coalesced loads).
+//   * Fast path (k <= 256): the radix select first runs over the per-thread maxima, one
+//     key per thread, and T is the prefix it settles on with its lower bits clear.  T is
+//     at most the k-th largest maximum, which is at most the k-th largest key (k distinct
+//     maxima are at least as large), so every selected key, ties included, is >= T.  The
+//     keys >= T (a few hundred on most inputs) are gathered in LDS and the radix select
+//     runs again over at most 4 per thread.  Both of its runs touch far fewer keys than
+//     one pass over all of them, whose LDS histogram atomics dominate the full path.
+//   * Otherwise (or when more than kTopkCap keys are >= T, as with many equal scores) the
+//     radix select runs over all the keys.
+// The selection is then two LDS bitmaps over the pages (keys above the selected bucket,
+// keys equal to it): equal keys are taken lowest pages first, and the result is compacted
+// in ascending page order.  Fewer than k pages: all of them, padded with -1.
+constexpr int kTopkCap = 1024;
 template <int KPT>
 __global__ void __launch_bounds__(256) topk_kernel(const LosaArgs a, const double* scores, int32_t* topk_pages) {
   constexpr int NW = 4 * KPT;                   // 64-page words of the bitmaps
-  __shared__ int hist[256];
-  __shared__ int tmp[4];
-  __shared__ int s_digit, s_above, s_count;
-  __shared__ unsigned long long s_and, s_or;
+  constexpr int KC = kTopkCap / 256;            // candidate slots per thread
+  __shared__ TopkShared sh;
   __shared__ uint64_t gt_bits[NW], eq_bits[NW];
+  __shared__ uint64_t c_key[kTopkCap];
+  __shared__ int c_page[kTopkCap];
   const int rid = blockIdx.x;                   // (b * h_q + h) * n_active + ai
   const int b = rid / (a.h_q * a.n_active);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -380,84 +477,73 @@ __global__ void __launch_bounds__(256) topk_kernel(const LosaArgs a, const doubl
   for (int j = 0; j < KPT; ++j) raw[j] = sc[min(tid + 256 * j, P - 1)];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) key[j] = tid + 256 * j < P ? order_key(raw[j]) : 0ull;
-  if (tid == 0) {
-    s_and = ~0ull;
-    s_or = 0ull;
+  for (int i = tid; i < NW; i += 256) {
+    gt_bits[i] = 0ull;
+    eq_bits[i] = 0ull;
   }
-  __syncthreads();
-  {
-    uint64_t ka = ~0ull, ko = 0ull;
+
+  // ---- fast path: candidates >= T ----------------------------------------------------
+  bool fast = false;
+  uint64_t prefix = 0, pmask = 0;
+  int need = 0;
+  if (K <= 256) {
+    // thread t has keys iff t < P, and P > K: at least K maxima
+    uint64_t mt[1] = {0ull};
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-      if (tid + 256 * j < P) {
-        ka &= key[j];
-        ko |= key[j];
+      if (tid + 256 * j < P) mt[0] = key[j] > mt[0] ? key[j] : mt[0];
+    uint64_t tprefix, tmask;
+    int tneed;
+    radix_select<1>(mt, P < 256 ? P : 256, K, sh, tprefix, tmask, tneed);
+    {
+      const uint64_t T = tprefix;   // the bits below tmask are clear
+      int c = 0;
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) c += tid + 256 * j < P && key[j] >= T ? 1 : 0;
+      int total;
+      int o = block_incl_scan(c, sh.tmp, &total) - c;
+      if (total <= kTopkCap) {   // uniform
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+          if (tid + 256 * j < P && key[j] >= T) {
+            c_key[o] = key[j];
+            c_page[o] = tid + 256 * j;
+            ++o;
+          }
+        __syncthreads();
+        uint64_t ck[KC];
+        int cpg[KC];
+#pragma unroll
+        for (int i = 0; i < KC; ++i) {
+          const int idx = tid + 256 * i;
+          ck[i] = idx < total ? c_key[idx] : 0ull;
+          cpg[i] = idx < total ? c_page[idx] : 0;
+        }
+        radix_select<KC>(ck, total, K, sh, prefix, pmask, need);
+#pragma unroll
+        for (int i = 0; i < KC; ++i) {
+          if (tid + 256 * i >= total) continue;
+          const uint64_t km = ck[i] & pmask;
+          const unsigned long long bit = 1ull << (cpg[i] & 63);
+          if (km > prefix) atomicOr((unsigned long long*)&gt_bits[cpg[i] >> 6], bit);
+          else if (km == prefix) atomicOr((unsigned long long*)&eq_bits[cpg[i] >> 6], bit);
+        }
+        fast = true;
       }
-    ka = wave_and64(ka);
-    ko = wave_or64(ko);
-    if (lane == 0) {
-      atomicAnd(&s_and, (unsigned long long)ka);
-      atomicOr(&s_or, (unsigned long long)ko);
     }
   }
-  __syncthreads();
-  const uint64_t diff = s_and ^ s_or;
-  int pass0 = 0;
-  while (pass0 < 8 && ((diff >> (56 - 8 * pass0)) & 255) == 0) ++pass0;
-  uint64_t pmask = pass0 == 0 ? 0ull : (pass0 == 8 ? ~0ull : ~0ull << (64 - 8 * pass0));
-  uint64_t prefix = s_and & pmask;
-  int need = K;
-  for (int pass = pass0; pass < 8; ++pass) {
-    const int shift = 56 - 8 * pass;
-    hist[tid] = 0;
-    __syncthreads();
-    // when every matching lane of a wave has the same digit (common in the leading
-    // passes) the wave adds its count with one atomic
+  if (!fast) {
+    // ---- all keys -----------------------------------------------------------------------
+    radix_select<KPT>(key, P, K, sh, prefix, pmask, need);
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const bool match = tid + 256 * j < P && (key[j] & pmask) == prefix;
-      const int dg = (int)((key[j] >> shift) & 255);
-      const uint64_t m = __ballot(match);
-      if (m) {
-        const int leader = __ffsll((unsigned long long)m) - 1;
-        const int ldg = __builtin_amdgcn_readlane(dg, leader);
-        if (__ballot(match && dg == ldg) == m) {
-          if (lane == leader) atomicAdd(&hist[ldg], (int)__popcll(m));
-        } else if (match) {
-          atomicAdd(&hist[dg], 1);
-        }
+      const bool ok = tid + 256 * j < P;
+      const uint64_t km = key[j] & pmask;
+      const uint64_t g = __ballot(ok && km > prefix), e = __ballot(ok && km == prefix);
+      if (lane == 0) {
+        gt_bits[4 * j + w] = g;
+        eq_bits[4 * j + w] = e;
       }
-    }
-    __syncthreads();
-    // thread t looks at digit 255 - t: inclusive count of keys with a digit >= 255 - t
-    const int c = hist[255 - tid];
-    int total;
-    const int cum = block_incl_scan(c, tmp, &total);
-    if (cum >= need && cum - c < need) {
-      s_digit = 255 - tid;
-      s_above = cum - c;
-      s_count = c;
-    }
-    __syncthreads();
-    need -= s_above;
-    prefix |= (uint64_t)s_digit << shift;
-    pmask |= (uint64_t)255 << shift;
-    const bool whole = s_count == need;          // the bucket is exactly what is still needed
-    __syncthreads();
-    if (whole) break;
-  }
-  // Selected: keys above the bucket (prefix bits greater) and `need` keys of the bucket,
-  // lowest pages first (the whole bucket when the passes stopped early; equal full keys
-  // otherwise).
-  const uint64_t T = prefix;
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const bool valid = tid + 256 * j < P;
-    const uint64_t km = key[j] & pmask;
-    const uint64_t g = __ballot(valid && km > T), e = __ballot(valid && km == T);
-    if (lane == 0) {
-      gt_bits[4 * j + w] = g;
-      eq_bits[4 * j + w] = e;
     }
   }
   __syncthreads();
@@ -465,7 +551,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const LosaArgs a, const doubl
   const int wi = tid < NW ? tid : 0;
   const uint64_t eqw = tid < NW ? eq_bits[wi] : 0ull;
   int total;
-  const int eq_before = block_incl_scan(__popcll(eqw), tmp, &total) - __popcll(eqw);
+  const int eq_before = block_incl_scan(__popcll(eqw), sh.tmp, &total) - __popcll(eqw);
   uint64_t take = 0ull;
   {
     int left = need - eq_before;
@@ -478,7 +564,7 @@ __global__ void __launch_bounds__(256) topk_kernel(const LosaArgs a, const doubl
     }
   }
   const uint64_t selw = (tid < NW ? gt_bits[wi] : 0ull) | take;
-  int pos = block_incl_scan(__popcll(selw), tmp, &total) - __popcll(selw);
+  int pos = block_incl_scan(__popcll(selw), sh.tmp, &total) - __popcll(selw);
   uint64_t m = selw;
   while (m) {
     const int bit = __ffsll((unsigned long long)m) - 1;
