@@ -143,6 +143,26 @@ def test_topk_ties_go_to_lower_pages(gpu_lib):
     assert np_of(out["topk"]).max() < 40
 
 
+def test_topk_all_scores_equal_take_the_lowest_pages(gpu_lib):
+    """Every page holds the same keys, so all 2000 page scores are equal: more keys pass the
+    top-k threshold than the candidate buffer holds, the selection runs over all keys, and
+    each row takes the lowest pages (bit-exact with the oracle)."""
+    import torch
+    fb = gpu_lib
+    say("[losa] top-k with 2000 equal page scores")
+    p = synth.custom(8, 1, 2, 2, 64, 8, [16 * 2000], std=1.0)
+    p.k = np.tile(p.k[:16], (2000, 1, 1))
+    q_prev = p.q
+    q_cur = synth.round_bf16(p.q + 0.5 * synth.rng(9).standard_normal(p.q.shape, dtype=np.float32))
+    dev, s, ls, out = _setup(fb, p, q_cur, q_prev, 3, 16, 64)
+    fb.losa_select_union(ls, dev["q_cur"], dev["q_prev"], dev["kmin"], dev["kmax"], out["active"], out["topk"],
+                         out["union"], out["count"], out["ws"])
+    torch.cuda.synchronize()
+    exp = OL.select_union(q_cur, q_prev, p.k, p.cu, 2, 3, 16, 64)
+    assert (exp["topk"] == np.arange(64)).all()
+    _check_selection(p, out, exp, 3)
+
+
 @pytest.mark.parametrize("B", [16, 300])
 def test_active_set_ties_go_to_lower_tokens(gpu_lib, B):
     """Unchanged queries give every block token the locality score 0: the active set is
