@@ -207,7 +207,7 @@ __global__ void __launch_bounds__(256) active_kernel(const LosaArgs a, const dou
 //   acc + q * (q >= 0 ? kmax : kmin) == fma(q-, kmin, fma(q+, kmax, acc))
 // exactly: one of the two products is zero, the other is exact in fp64 and rounds once, as
 // in the left-to-right fp64 sum over d of the definition.
-constexpr int kQpp = 4;
+constexpr int kQpp = 2;   // pages per thread: 114 VGPRs, 4 waves per SIMD (4 pages: 202, 2 waves, 4 us slower per step)
 constexpr int kRankInQuest = 256;   // blocks up to this size rank their active set inside the QUEST launch
 constexpr int kQRow = 257;   // LDS row stride (pairs): the two half-waves' rows fall in different banks
 template <bool BF16>
