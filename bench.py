@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only-main", action="store_true", help="headline workload only (for profiling)")
+    ap.add_argument("--only-others", action="store_true",
+                    help="ragged-GQA and LoSA sparse steps only, one JSON line of their times (for profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (counter calibration)")
@@ -301,6 +303,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.only_others:
+        print(json.dumps({"only_others": only_others(fb, args)}))
+        return
 
     # ---------------------------------------------------------------- headline workload
     p = synth.dllm()
@@ -579,28 +585,9 @@ def other_workloads(fb, args):
                           "fresh_heads": n_fresh, "tokens_per_s": nq / w_m}
     del dev, bufs
     # LoSA sparse step
-    p = synth.losa()
-    dev = to_device(p)
-    shape, bufs = setup_step(fb, p, dev)
-    ls = fb.make_losa_shape(shape, page_size=16, topk=64, n_active=8)
-    el = 2
-    kmin = torch.empty(fb.losa_meta_bytes(ls) // el, dtype=torch.bfloat16, device="cuda")
-    kmax = torch.empty_like(kmin)
-    fb.losa_page_meta(ls, dev["k"], kmin, kmax)
-    qc, qp = tensor(p.extra["q_cur"]), tensor(p.extra["q_prev"])
-    cap = fb.losa_union_capacity(ls)
-    sel = dict(active=torch.empty((1, 8), dtype=torch.int32, device="cuda"),
-               topk=torch.empty((1, 32, 8, 64), dtype=torch.int32, device="cuda"),
-               union=torch.empty((1, 32, cap), dtype=torch.int32, device="cuda"),
-               count=torch.empty((1, 32), dtype=torch.int32, device="cuda"),
-               ws=torch.empty(fb.losa_workspace_size(ls), dtype=torch.uint8, device="cuda"))
+    p, dev, shape, bufs, ls, sparse, sel, cap = losa_setup(fb)
     fresh = torch.full((1,), 1 << 30, dtype=torch.int32, device="cuda")
     w_d, _, _ = time_steps(lambda tr: run_step(fb, shape, dev, bufs, fresh, trace=tr), steps, 2)
-
-    def sparse(tr):
-        fb.losa_step(ls, qc, qp, dev["k"], dev["v"], dev["k_blk"], dev["v_blk"], kmin, kmax, bufs["ca"], bufs["cl"],
-                     bufs["af"], bufs["lf"], sel["active"], sel["topk"], sel["union"], sel["count"], sel["ws"],
-                     trace=tr)
     # a short step (about 0.1 ms): the full step count and more warm-up, as for the dLLM steps
     w_s, a_s, _ = time_steps(sparse, args.steps, 5)
     cnt = sel["count"].cpu().numpy()
@@ -611,9 +598,55 @@ def other_workloads(fb, args):
                           "alg_bytes": meta_bytes + union_bytes,
                           "frac_hbm_step": (meta_bytes + union_bytes) / w_s / 1e9 / HBM_PEAK_GBS}
     out["sparse_residual"] = residual_workload(fb, p, dev, shape, sel, cap, steps, args.steps)
-    del dev, bufs, kmin, kmax
+    del dev, bufs, sparse   # the step's closure holds the page metadata
     out["multi_branch_varlen"] = varlen_workload(fb, args)
     return out
+
+
+def losa_setup(fb):
+    """The LoSA workload (131072-token prefix, 32 heads, B 64, pages of 16, |A| 8, top-64):
+    device inputs, page metadata, selection buffers, and the sparse step as a callable."""
+    import torch
+    import synth
+    from synth.device import to_device, tensor
+    p = synth.losa()
+    dev = to_device(p)
+    shape, bufs = setup_step(fb, p, dev)
+    ls = fb.make_losa_shape(shape, page_size=16, topk=64, n_active=8)
+    kmin = torch.empty(fb.losa_meta_bytes(ls) // 2, dtype=torch.bfloat16, device="cuda")
+    kmax = torch.empty_like(kmin)
+    fb.losa_page_meta(ls, dev["k"], kmin, kmax)
+    qc, qp = tensor(p.extra["q_cur"]), tensor(p.extra["q_prev"])
+    cap = fb.losa_union_capacity(ls)
+    sel = dict(active=torch.empty((1, 8), dtype=torch.int32, device="cuda"),
+               topk=torch.empty((1, 32, 8, 64), dtype=torch.int32, device="cuda"),
+               union=torch.empty((1, 32, cap), dtype=torch.int32, device="cuda"),
+               count=torch.empty((1, 32), dtype=torch.int32, device="cuda"),
+               ws=torch.empty(fb.losa_workspace_size(ls), dtype=torch.uint8, device="cuda"))
+
+    def sparse(tr):
+        fb.losa_step(ls, qc, qp, dev["k"], dev["v"], dev["k_blk"], dev["v_blk"], kmin, kmax, bufs["ca"], bufs["cl"],
+                     bufs["af"], bufs["lf"], sel["active"], sel["topk"], sel["union"], sel["count"], sel["ws"],
+                     trace=tr)
+    return p, dev, shape, bufs, ls, sparse, sel, cap
+
+
+def only_others(fb, args):
+    """Profiling mode: the ragged-GQA fresh step and the LoSA sparse step, `steps` times each
+    after `warmup`, for counter runs on the kernels other than the dLLM step's."""
+    import torch
+    import synth
+    from synth.device import to_device
+    p = synth.ragged()
+    dev = to_device(p)
+    shape, bufs = setup_step(fb, p, dev, varlen=True)
+    fresh = torch.full((p.batch,), 1 << 30, dtype=torch.int32, device="cuda")
+    w_r = wall_time(lambda tr: run_step(fb, shape, dev, bufs, fresh), args.steps, args.warmup)
+    del dev, bufs
+    _, _, _, _, _, sparse, sel, _ = losa_setup(fb)
+    w_s = wall_time(sparse, args.steps, args.warmup)
+    return {"ragged_fresh_step_us": w_r * 1e6, "losa_sparse_step_us": w_s * 1e6,
+            "union_pages": int(sel["count"].sum().item())}
 
 
 def residual_workload(fb, p, dev, shape, sel, cap, steps, short_steps):
