@@ -69,6 +69,8 @@ SMALL = [
     # launch of its own above that
     ("block256_rank_in_quest", 1, 2, 2, 64, 256, [400], 7, 16, 5, "bf16"),
     ("block300_rank_own_launch", 1, 2, 2, 64, 300, [500], 5, 16, 6, "bf16"),
+    # top-k above 256: the selection runs over all keys (no threshold from the thread maxima)
+    ("topk300_over_all_keys", 1, 2, 2, 64, 8, [1000], 2, 1, 300, "bf16"),
 ]
 
 
