@@ -5,13 +5,13 @@
 namespace fb {
 
 // One wave per output row (b, i, h); lanes own dims lane + 64 e.
-template <int E, int UP, int UB>
+template <int E, int UP, int UB, bool DECIDE>
 __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs C) {
   const int lane = threadIdx.x & 63;
   const int rowid = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   if (rowid >= C.batch * C.B * C.h_q) return;
   RowState<E, UP, UB> st;
-  row_issue<E, UP, UB>(C, rowid, lane, st);
+  row_issue<E, UP, UB, DECIDE>(C, rowid, lane, st);
   if (st.valid) row_finish<E, UP, UB>(C, lane, st);
 }
 
@@ -139,6 +139,8 @@ hipError_t launch_sim_reduce(int32_t batch, int32_t B, int32_t h_q, const double
   return hipGetLastError();
 }
 
+constexpr int64_t kCombineDecideRows = 16384;
+
 hipError_t launch_combine(const CombineArgs& c, hipStream_t st) {
   const int64_t rows = (int64_t)c.batch * c.B * c.h_q;
   if (rows == 0) return hipSuccess;
@@ -156,14 +158,20 @@ hipError_t launch_combine(const CombineArgs& c, hipStream_t st) {
   // chunk loads issued up front: as many as the plan has (d = 128), else 8
   const int up = c.p_splits <= 1 ? 1 : c.p_splits <= 2 ? 2 : c.p_splits <= 4 ? 4 : 8;
   const bool ub1 = c.b_splits <= 1;
+  // a large step combine is bound by its bytes: the rows read the reuse decision first (or
+  // know it, with no mask and no count) and load only what they use; a small one is bound
+  // by latency and loads everything at once
+  const bool decide = c.mode == kModeStep && rows > kCombineDecideRows;
   if (c.d <= 64) {
-    hipLaunchKernelGGL((combine_kernel<1, 8, 8>), grid, dim3(256), 0, st, c);
+    hipLaunchKernelGGL((combine_kernel<1, 8, 8, false>), grid, dim3(256), 0, st, c);
   } else if (c.d <= 128) {
 #define FB_COMBINE_UB(UP)                                                                    \
-  if (ub1)                                                                                   \
-    hipLaunchKernelGGL((combine_kernel<2, UP, 1>), grid, dim3(256), 0, st, c);               \
+  if (ub1 && decide)                                                                         \
+    hipLaunchKernelGGL((combine_kernel<2, UP, 1, true>), grid, dim3(256), 0, st, c);         \
+  else if (ub1)                                                                              \
+    hipLaunchKernelGGL((combine_kernel<2, UP, 1, false>), grid, dim3(256), 0, st, c);        \
   else                                                                                       \
-    hipLaunchKernelGGL((combine_kernel<2, UP, 8>), grid, dim3(256), 0, st, c);
+    hipLaunchKernelGGL((combine_kernel<2, UP, 8, false>), grid, dim3(256), 0, st, c);
     if (up == 1) {
       FB_COMBINE_UB(1)
     } else if (up == 2) {
@@ -175,7 +183,7 @@ hipError_t launch_combine(const CombineArgs& c, hipStream_t st) {
     }
 #undef FB_COMBINE_UB
   } else {
-    hipLaunchKernelGGL((combine_kernel<4, 8, 8>), grid, dim3(256), 0, st, c);
+    hipLaunchKernelGGL((combine_kernel<4, 8, 8, false>), grid, dim3(256), 0, st, c);
   }
   return hipGetLastError();
 }

@@ -153,8 +153,10 @@ struct RowState {
 };
 
 // UP / UB: prefix / block chunks whose loads are issued up front (further chunks, if
-// any, are read during the reduction).
-template <int E, int UP, int UB>
+// any, are read during the reduction).  DECIDE: read the reuse decision first and load
+// only what the row uses (the prefix chunks of a recomputed row, the cached row of a
+// reused one): one more round trip, but a large combine moves a third fewer bytes.
+template <int E, int UP, int UB, bool DECIDE = false>
 __device__ __forceinline__ void row_issue(const CombineArgs& C, int rowid, int lane, RowState<E, UP, UB>& st) {
   const int h = rowid % C.h_q;
   const int i = (rowid / C.h_q) % C.B;
@@ -189,15 +191,26 @@ __device__ __forceinline__ void row_issue(const CombineArgs& C, int rowid, int l
     st.prow = jg * C.n_active + (pos < 0 ? 0 : pos);
   }
 
-  // every partial load
+  // the reuse inputs: read first with DECIDE, else while the partials are in flight
+  auto read_reuse = [&]() {
+    if (C.mode != kModeLosa) {
+      if (C.m_upd)
+        st.fresh = C.m_upd[b] >= C.tau;
+      else if (C.mask)
+        st.fresh = C.mask[b * C.h_q + h] == 0;
+    }
+  };
+  if constexpr (DECIDE) read_reuse();
+
+  // the partial loads (all of them without DECIDE)
   st.pslot0 = (int64_t)(b * C.h_kv + hk) * C.p_splits;
   st.bslot0 = (int64_t)(b * C.h_kv + hk) * C.b_splits;
   st.cached_l = kNegInf;
-  if (has_prefix && C.p_splits > 0)
+  if (has_prefix && C.p_splits > 0 && (!DECIDE || st.fresh))
     issue_partials<E, UP>(C.po, C.pml, st.pslot0, C.p_rows, st.prow, C.p_splits, d, lane, st.PP);
   if (C.mode != kModePrefixOnly && C.b_splits > 0)
     issue_partials<E, UB>(C.bo, C.bml, st.bslot0, C.b_rows, jg * C.B + i, C.b_splits, d, lane, st.PB);
-  if (has_prefix && C.mode != kModePrefixOnly) {
+  if (has_prefix && C.mode != kModePrefixOnly && (!DECIDE || !st.fresh || C.sim_parts)) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int dd = lane + 64 * e;
@@ -205,14 +218,7 @@ __device__ __forceinline__ void row_issue(const CombineArgs& C, int rowid, int l
     }
     st.cached_l = C.cache_l[rowid];
   }
-
-  // reuse inputs, read while the partials are in flight
-  if (C.mode != kModeLosa) {
-    if (C.m_upd)
-      st.fresh = C.m_upd[b] >= C.tau;
-    else if (C.mask)
-      st.fresh = C.mask[b * C.h_q + h] == 0;
-  }
+  if constexpr (!DECIDE) read_reuse();
   st.nk = C.n_uniform;
   if (C.page_count)
     st.nk = C.page_count[b * C.h_kv + hk] * C.page_size;

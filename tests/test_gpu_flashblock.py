@@ -198,12 +198,15 @@ def test_tiny_f32_two_steps(gpu_lib):
     check_lse(np_of(o["l_full"]), rl, "f32", "tiny reuse L_full")
 
 
-def test_reuse_equals_recompute_bitwise(gpu_lib):
+@pytest.mark.parametrize("block", [32, 1056], ids=["block32", "block1056_combine_decides_first"])
+def test_reuse_equals_recompute_bitwise(gpu_lib, block):
     """Unchanged queries, KV and cache: the reuse step and the recompute step give
-    bit-identical A_full, L_full and cache."""
+    bit-identical A_full, L_full and cache.  At block 1056 (16896 rows) the combine reads
+    each row's decision before its loads; the threshold rule is checked there too."""
     import torch
     fb = gpu_lib
-    p = synth.custom(5, 2, 8, 2, 128, 32, [2000, 777])
+    say(f"[reuse bitwise] block {block}")
+    p = synth.custom(5, 2, 8, 2, 128, block, [2000, 777])
     dev = to_device(p)
     shape = _shape(fb, p, dev, varlen=True)
     ws = _ws(fb, shape)
@@ -227,6 +230,13 @@ def test_reuse_equals_recompute_bitwise(gpu_lib):
     fb.step(*args(mixed))
     torch.cuda.synchronize()
     assert torch.equal(o["a_full"], a0)
+    # counts 9 and 0 with tau 4: sequence 0 recomputes, sequence 1 reuses
+    m = torch.tensor([9, 0], dtype=torch.int32, device="cuda")
+    fb.step_threshold(shape, dev["q"], dev["k"], dev["v"], dev["k_blk"], dev["v_blk"], m, 4, o["cache_a"],
+                      o["cache_l"], o["a_full"], o["l_full"], ws)
+    torch.cuda.synchronize()
+    for x, y in ((o["a_full"], a0), (o["l_full"], l0), (o["cache_a"], c0), (o["cache_l"], cl0)):
+        assert torch.equal(x, y)
 
 
 def test_threshold_block_of_steps(gpu_lib):

@@ -169,6 +169,36 @@ def test_block_run_similarity(gpu_lib):
     _check_run(got, exp, "similarity")
 
 
+def test_block_run_similarity_large_block(gpu_lib):
+    """Block 2100 with 8 heads (16800 rows, past the size where the combine reads each
+    row's decision before its loads): the similarity after step 1 is the cosine between
+    the block-external outputs of steps 0 and 1 (computed here by two prefix passes), so
+    a fresh row still reads its cached row; the cache ends as step 1's prefix output."""
+    import torch
+    from oracle.flashblock import head_cosine
+    fb = gpu_lib
+    p = synth.custom(61, 1, 8, 2, 128, 2100, [1500], std=1.0)
+    dev = to_device(p)
+    s = _shape(fb, p, dev, False)
+    q, kb, vb = _step_inputs(p, 2, 62, [1e-3, 1.0] * 4)
+    plan = fb.BlockPlan(2, fb.FB_RULE_SIMILARITY, 0, 0.95)
+    say("[block] similarity, block 2100")
+    got = _run_block(fb, s, plan, dev, q, kb, vb, None, dev["k"], dev["v"])
+    ws = torch.empty(max(fb.workspace_size(s), 16), dtype=torch.uint8, device="cuda")
+    outs = []
+    for t in range(2):
+        a = torch.empty(p.q.shape, dtype=torch.float32, device="cuda")
+        l = torch.empty(p.q.shape[:3], dtype=torch.float32, device="cuda")
+        fb.prefix_attn(s, tensor(q[t]), dev["k"], dev["v"], a, l, ws)
+        torch.cuda.synchronize()
+        outs.append(np_of(a))
+    assert not got["masks"].any()          # no mask before step 2: every head recomputes
+    assert np.isnan(got["sims"][0]).all()
+    exp = head_cosine(outs[0], outs[1])
+    assert np.max(np.abs(got["sims"][1] - exp)) <= 1e-5, (got["sims"][1], exp)
+    assert np.max(np.abs(got["ca"] - outs[1]) / (1.0 + np.abs(outs[1]))) <= 1e-5
+
+
 def test_three_blocks(gpu_lib):
     """A multi-block run: the steps of a block under the threshold rule, then the block's
     last K/V appended to the prefix, three times; each block against the oracle chain."""
