@@ -14,7 +14,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libflashblock.so")
 
 FB_BF16, FB_F32 = 0, 1
-STATUS = {0: "FB_OK", 1: "FB_ERR_INVALID_ARG", 2: "FB_ERR_UNSUPPORTED", 3: "FB_ERR_WORKSPACE", 5: "FB_ERR_HIP"}
+STATUS = {0: "FB_OK", 1: "FB_ERR_INVALID_ARG", 2: "FB_ERR_UNSUPPORTED", 3: "FB_ERR_WORKSPACE",
+          4: "FB_ERR_CACHE_INVALID", 5: "FB_ERR_HIP"}
+FB_FLAG_CHECK_CACHE = 1   # fb_shape.flags: debug check that every reused cache row was written
 EXPORTS = ("fb_status_string", "fb_workspace_size", "fb_prefix_attn", "fb_block_attn", "fb_lse_merge",
            "fb_step", "fb_step_threshold", "fb_mask_threshold", "fb_mask_similarity", "fb_head_cosine", "losa_meta_bytes",
            "losa_workspace_size", "losa_union_capacity", "losa_page_meta", "losa_select_union", "losa_step",

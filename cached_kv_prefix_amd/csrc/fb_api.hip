@@ -33,7 +33,7 @@ fb_status check_shape(const fb_shape* s) {
   if (!s) return FB_ERR_INVALID_ARG;
   if (s->batch < 1 || s->h_q < 1 || s->h_kv < 1 || s->head_dim < 1 || s->block < 1) return FB_ERR_INVALID_ARG;
   if (s->h_q % s->h_kv != 0) return FB_ERR_INVALID_ARG;
-  if (s->flags != 0 || s->num_splits < 0) return FB_ERR_INVALID_ARG;
+  if ((s->flags & ~FB_FLAG_CHECK_CACHE) != 0 || s->num_splits < 0) return FB_ERR_INVALID_ARG;
   if (!(s->softmax_scale >= 0.f) || !isfinite(s->softmax_scale)) return FB_ERR_INVALID_ARG;
   if (s->cu_seqlens_k ? s->max_seqlen_k < 0 : s->seqlen_k < 0) return FB_ERR_INVALID_ARG;
   if (s->dtype == FB_BF16) {
@@ -154,12 +154,13 @@ Region partial_region(const fb_shape* s, const RowPlan& rp, const SplitPlan& sp,
   return r;
 }
 
-// Full plan of the dense step (prefix source 0, block source 1).
+// Full plan of the dense step (prefix source 0, block source 1); the last 256 bytes hold
+// the flag of the debug cache check.
 struct StepPlan {
   RowPlan rp;
   SplitPlan pre, blk;
   Region rpre, rblk;
-  size_t ws_bytes;
+  size_t check_off, ws_bytes;
 };
 StepPlan step_plan(const fb_shape* s) {
   StepPlan p;
@@ -169,7 +170,8 @@ StepPlan step_plan(const fb_shape* s) {
   p.pre = split_plan(s, p.rp, max_prefix(s), s->num_splits, blk_items);
   p.rpre = partial_region(s, p.rp, p.pre, 0);
   p.rblk = partial_region(s, p.rp, p.blk, p.rpre.bytes);
-  p.ws_bytes = p.rpre.bytes + p.rblk.bytes;
+  p.check_off = align256(p.rpre.bytes + p.rblk.bytes);
+  p.ws_bytes = p.check_off + 256;
   return p;
 }
 
@@ -246,6 +248,21 @@ inline void rec(hipEvent_t e, hipStream_t st) {
 
 fb_status hip_status(hipError_t e) { return e == hipSuccess ? FB_OK : FB_ERR_HIP; }
 
+// FB_FLAG_CHECK_CACHE: whether every cache row the call would reuse has been written (a
+// never-written row holds NaN in cache_l).  Runs before the call's own launches, writes
+// only the flag in the workspace, and waits for it on the host.
+fb_status check_cache(const fb_shape* s, const float* cache_l, const uint8_t* mask, const int32_t* m_upd,
+                      int32_t tau, bool all_rows, void* flag, hipStream_t stream) {
+  if (!(s->flags & FB_FLAG_CHECK_CACHE) || (!all_rows && !mask && !m_upd)) return FB_OK;
+  int32_t* bad = (int32_t*)flag;
+  hipError_t e = launch_cache_check(cache_l, s->batch, s->block, s->h_q, mask, m_upd, tau, all_rows, bad, stream);
+  int32_t host = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&host, bad, sizeof(host), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return FB_ERR_HIP;
+  return host ? FB_ERR_CACHE_INVALID : FB_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -256,6 +273,7 @@ const char* fb_status_string(fb_status s) {
     case FB_ERR_INVALID_ARG: return "invalid argument";
     case FB_ERR_UNSUPPORTED: return "unsupported configuration";
     case FB_ERR_WORKSPACE: return "workspace too small";
+    case FB_ERR_CACHE_INVALID: return "a reused cache row was never written";
     case FB_ERR_HIP: return "HIP runtime error";
   }
   return "unknown status";
@@ -325,6 +343,8 @@ fb_status run_step(const fb_shape* s, const void* q, const void* k, const void* 
   if (!cache_a || !cache_l || !a_full) return FB_ERR_INVALID_ARG;
   const StepPlan p = step_plan(s);
   if (ws_bytes < p.ws_bytes || (p.ws_bytes && (!ws || !aligned16(ws)))) return FB_ERR_WORKSPACE;
+  if ((st = check_cache(s, cache_l, reuse_mask, m_upd, tau, false, (char*)ws + p.check_off, stream)) != FB_OK)
+    return st;
   AttnArgs a = base_args(s, q);
   a.src0 = make_src(p.rp, p.pre, k, v, s->cu_seqlens_k, s->seqlen_k, (float*)ws, p.rpre);
   a.src0.mask = reuse_mask;
@@ -439,7 +459,7 @@ struct LosaPlan {
   RowPlan rp_sparse;
   SplitPlan sp_sparse;
   Region r_sparse, r_block;
-  size_t scores_off, active_off, loc_off, ws_bytes;
+  size_t scores_off, active_off, loc_off, check_off, ws_bytes;
 };
 LosaPlan losa_plan(const losa_shape* ls) {
   LosaPlan p;
@@ -453,7 +473,8 @@ LosaPlan losa_plan(const losa_shape* ls) {
   const size_t scores = (size_t)s->batch * s->h_q * ls->n_active * ls->max_pages * sizeof(double);
   p.active_off = align256(p.scores_off + scores);
   p.loc_off = align256(p.active_off + (size_t)s->batch * ls->n_active * sizeof(int32_t));
-  p.ws_bytes = align256(p.loc_off + (size_t)s->batch * s->block * sizeof(double));
+  p.check_off = align256(p.loc_off + (size_t)s->batch * s->block * sizeof(double));
+  p.ws_bytes = p.check_off + 256;
   return p;
 }
 
@@ -524,6 +545,10 @@ fb_status losa_step(const losa_shape* ls, const void* q_cur, const void* q_prev,
     return FB_ERR_INVALID_ARG;
   const LosaPlan p = losa_plan(ls);
   if (ws_bytes < p.ws_bytes || !ws || !aligned16(ws)) return FB_ERR_WORKSPACE;
+  // stable rows (every block with |A| < B has some) reuse their cached rows
+  if ((st = check_cache(s, cache_l, nullptr, nullptr, 0, ls->n_active < s->block, (char*)ws + p.check_off,
+                        stream)) != FB_OK)
+    return st;
 
   rec(trace ? trace->select_begin : nullptr, stream);
   st = run_selection(ls, p, q_cur, q_prev, kmin, kmax, active, topk_pages, union_pages, union_count, ws, stream);
@@ -601,7 +626,7 @@ struct ResidualPlan {
   RowPlan rp;
   SplitPlan sel, comp, blk;
   Region rsel, rcomp, rblk;
-  size_t pages_off, count_off, ws_bytes;
+  size_t pages_off, count_off, check_off, ws_bytes;
 };
 ResidualPlan residual_plan(const fb_residual_shape* rs) {
   ResidualPlan p;
@@ -617,7 +642,8 @@ ResidualPlan residual_plan(const fb_residual_shape* rs) {
   const size_t groups = (size_t)s->batch * s->h_kv;
   p.pages_off = p.rsel.bytes + p.rcomp.bytes + p.rblk.bytes;
   p.count_off = align256(p.pages_off + groups * rs->max_pages * sizeof(int32_t));
-  p.ws_bytes = align256(p.count_off + groups * sizeof(int32_t));
+  p.check_off = align256(p.count_off + groups * sizeof(int32_t));
+  p.ws_bytes = p.check_off + 256;
   return p;
 }
 
@@ -643,6 +669,8 @@ fb_status fb_residual_step(const fb_residual_shape* rs, const void* q, const voi
   if (!sel_pages || !sel_count || !cache_a || !cache_l || !a_full) return FB_ERR_INVALID_ARG;
   const ResidualPlan p = residual_plan(rs);
   if (ws_bytes < p.ws_bytes || !ws || !aligned16(ws)) return FB_ERR_WORKSPACE;
+  if ((st = check_cache(s, cache_l, reuse_mask, nullptr, 0, false, (char*)ws + p.check_off, stream)) != FB_OK)
+    return st;
   int32_t* comp_pages = (int32_t*)((char*)ws + p.pages_off);
   int32_t* comp_count = (int32_t*)((char*)ws + p.count_off);
 

@@ -50,6 +50,24 @@ __global__ void __launch_bounds__(256) lse_merge_kernel(int64_t rows, int d, con
   if (lf_ && lane == 0) lf_[r] = lf;
 }
 
+// Debug check of the cache rows a step would reuse: *bad = 1 if any of them holds NaN in
+// cache_l (never written), else 0.  One workgroup scans every row, so the flag needs no
+// clearing beforehand.
+__global__ void __launch_bounds__(256) cache_check_kernel(const float* cache_l, int batch, int B, int h_q,
+                                                          const uint8_t* mask, const int32_t* m_upd, int tau,
+                                                          int all_rows, int32_t* bad) {
+  const int64_t rows = (int64_t)batch * B * h_q;
+  int found = 0;
+  for (int64_t r = threadIdx.x; r < rows; r += 256) {
+    const int h = (int)(r % h_q);
+    const int b = (int)(r / ((int64_t)B * h_q));
+    const bool reused = all_rows || (m_upd ? m_upd[b] < tau : mask ? mask[b * h_q + h] != 0 : false);
+    found |= reused && __builtin_isnan(cache_l[r]);
+  }
+  found = __syncthreads_or(found);
+  if (threadIdx.x == 0) *bad = found ? 1 : 0;
+}
+
 __global__ void mask_threshold_kernel(const int32_t* m, int tau, int batch, int h_q, uint8_t* mask) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)batch * h_q) return;
@@ -198,6 +216,13 @@ hipError_t launch_lse_merge(int64_t rows, int32_t d, const float* ao, const floa
     hipLaunchKernelGGL(lse_merge_kernel<2>, grid, dim3(256), 0, st, rows, d, ao, lo, ai, li, af, out_bf16, lf);
   else
     hipLaunchKernelGGL(lse_merge_kernel<4>, grid, dim3(256), 0, st, rows, d, ao, lo, ai, li, af, out_bf16, lf);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_check(const float* cache_l, int32_t batch, int32_t B, int32_t h_q, const uint8_t* mask,
+                              const int32_t* m_upd, int32_t tau, bool all_rows, int32_t* bad, hipStream_t st) {
+  hipLaunchKernelGGL(cache_check_kernel, dim3(1), dim3(256), 0, st, cache_l, batch, B, h_q, mask, m_upd, tau,
+                     all_rows ? 1 : 0, bad);
   return hipGetLastError();
 }
 

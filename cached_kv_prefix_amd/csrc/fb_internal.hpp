@@ -107,6 +107,9 @@ hipError_t launch_combine(const CombineArgs& c, hipStream_t st);
 hipError_t launch_lse_merge(int64_t rows, int32_t d, const float* ao, const float* lo,
                             const float* ai, const float* li, void* af, int out_bf16,
                             float* lf, hipStream_t st);
+// *bad = whether a row to be reused (all rows, or by mask / m_upd < tau) holds NaN in cache_l
+hipError_t launch_cache_check(const float* cache_l, int32_t batch, int32_t B, int32_t h_q, const uint8_t* mask,
+                              const int32_t* m_upd, int32_t tau, bool all_rows, int32_t* bad, hipStream_t st);
 hipError_t launch_mask_threshold(const int32_t* m, int32_t tau, int32_t batch, int32_t h_q,
                                  uint8_t* mask, hipStream_t st);
 hipError_t launch_mask_similarity(const float* sim, float gamma, int64_t n, uint8_t* mask,

@@ -23,7 +23,8 @@
  *   - Ownership: the caller allocates every buffer (inputs, outputs, cache, workspace) in
  *     device memory; the library allocates no device memory, keeps no state between calls
  *     and may be called concurrently on different streams with disjoint buffers.
- *   - Execution: all work is enqueued on `stream`; no call synchronises the host.
+ *   - Execution: all work is enqueued on `stream`; no call synchronises the host (but for
+ *     the debug check that FB_FLAG_CHECK_CACHE asks for).
  *   - Errors: arguments are checked on the host before anything is enqueued; on any
  *     error the call returns a non-zero fb_status and writes nothing.  A failed kernel
  *     launch returns FB_ERR_HIP.  No C++ exception crosses this interface.  Device-side
@@ -60,8 +61,22 @@ typedef enum fb_status {
   FB_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, h_q % h_kv != 0, ...      */
   FB_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. bf16 with head_dim 96)     */
   FB_ERR_WORKSPACE = 3,    /* ws_bytes smaller than the matching *_workspace_size()       */
+  FB_ERR_CACHE_INVALID = 4,/* FB_FLAG_CHECK_CACHE: a cache row the call would reuse has
+                              never been written (its cache_l entry is NaN)              */
   FB_ERR_HIP = 5           /* a HIP launch or runtime call failed                         */
 } fb_status;
+
+/* fb_shape.flags.
+ * FB_FLAG_CHECK_CACHE (debug): a cache row that has never been written is marked by NaN in
+ * cache_l (the caller fills a new cache's cache_l with NaN; every call that writes a row
+ * stores a number or -inf there).  With the flag set, fb_step, fb_step_threshold,
+ * fb_block_run, losa_step and fb_residual_step first check on the device every row the
+ * call would reuse: rows of heads whose reuse bit is 1 or whose sequence has M < tau, and
+ * for losa_step every row of a block that has stable rows (|A| < B).  If any of them holds
+ * NaN, the call returns FB_ERR_CACHE_INVALID and writes nothing but its workspace.  The
+ * check reads one flag back, so it synchronises `stream`: the one exception to the
+ * no-synchronisation rule, for debug runs only.  The other calls ignore the flag. */
+#define FB_FLAG_CHECK_CACHE 1u
 
 typedef enum fb_dtype { FB_BF16 = 0, FB_F32 = 1 } fb_dtype;
 
@@ -80,7 +95,7 @@ typedef struct fb_shape {
   float softmax_scale;         /* 0 selects 1/sqrt(head_dim)                              */
   int32_t num_splits;          /* prefix key chunks per sequence and KV head; 0 = chosen
                                   from the shape alone (deterministic for a given shape)   */
-  uint32_t flags;              /* must be 0                                               */
+  uint32_t flags;              /* 0 or FB_FLAG_CHECK_CACHE; other bits are invalid        */
 } fb_shape;
 
 /* Optional timing hooks: each non-null event is recorded on the call's stream right

@@ -31,6 +31,7 @@ def test_status_strings():
     lib = fb.load()
     assert lib.fb_status_string(0) == b"ok"
     assert lib.fb_status_string(3) == b"workspace too small"
+    assert lib.fb_status_string(4) == b"a reused cache row was never written"
     assert lib.fb_status_string(99) == b"unknown status"
 
 
@@ -92,7 +93,7 @@ def test_step_rejects_bad_pointers(over, code):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(h_kv=3), 1), (dict(batch=0), 1), (dict(block=0), 1), (dict(head_dim=96), 2),
-    (dict(flags=1), 1), (dict(num_splits=-1), 1), (dict(seqlen_k=-5), 1), (dict(softmax_scale=-1.0), 1),
+    (dict(flags=2), 1), (dict(flags=3), 1), (dict(num_splits=-1), 1), (dict(seqlen_k=-5), 1), (dict(softmax_scale=-1.0), 1),
     (dict(softmax_scale=float("inf")), 1), (dict(dtype=7), 1), (dict(dtype=fb.FB_F32, head_dim=512), 2),
 ])
 def test_step_rejects_bad_shapes(kw, code):
