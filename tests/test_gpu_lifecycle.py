@@ -132,7 +132,18 @@ def _check_run(got, exp, what):
         check_lse(got["lf"][s], exp["l_full"][s], "bf16", f"{what} L step {s}")
     fin = ~np.isnan(exp["sims"])
     assert np.isnan(got["sims"][~fin]).all()
-    assert np.max(np.abs(got["sims"][fin] - exp["sims"][fin])) <= 2e-4
+    # The cosine of two vectors moves by at most the angles their errors turn them through,
+    # arcsin(|dx| / |x|) + arcsin(|dy| / |y|).  The error of a cached A_out (mostly the bf16
+    # rounding of the probabilities in the PV product, whose pattern depends on the split
+    # layout) is measured per (sequence, head) on the final cache and taken as the scale of
+    # every step's cache, with a factor 2 for the steps not observed.
+    check_attn(got["ca"], exp["cache_a"], "bf16", f"{what} final cache")
+    ca, ea = got["ca"].astype(np.float64), exp["cache_a"]
+    rel = np.sqrt(((ca - ea) ** 2).sum(axis=(1, 3)) / (ea ** 2).sum(axis=(1, 3)))   # [b, h_q]
+    tol = 2 * 2 * np.arcsin(np.minimum(rel.max(), 1.0)) + 1e-6
+    err = np.max(np.abs(got["sims"][fin] - exp["sims"][fin]))
+    say(f"   {what}: similarity error {err:.2e}, bound {tol:.2e} (A_out relative error {rel.max():.2e})")
+    assert err <= tol
 
 
 def test_block_run_threshold(gpu_lib):
