@@ -7,7 +7,9 @@
  *   - a reuse step on unchanged inputs gives the fresh step's outputs bit for bit and
  *     leaves the cache untouched;
  *   - the threshold rule with a count at or above tau recomputes, bit for bit as fb_step;
- *   - a short workspace is refused before anything is written.
+ *   - a short workspace is refused before anything is written;
+ *   - with FB_FLAG_CHECK_CACHE, reusing a never-written cache (cache_l all NaN) is refused
+ *     with FB_ERR_CACHE_INVALID and nothing is written; recomputing everything runs.
  * Parity against the fp64 oracle is the Python suite's job; this program shows the
  * boundary on its own.  Prints one line per check and exits non-zero on a failure. */
 #include <math.h>
@@ -199,6 +201,25 @@ int main(void) {
     int untouched = 1;
     for (size_t i = 0; i < rows * d; ++i) untouched &= g_a[i] == 0x5a5a;
     check(untouched, "nothing was written");
+  }
+
+  /* debug cache check: a fresh cache (cache_l all NaN) may not be reused */
+  {
+    fb_shape sd = s;
+    sd.flags = FB_FLAG_CHECK_CACHE;
+    hip_ok(hipMemset(cache_l, 0xff, rows * 4), "NaN cache_l");   /* 0xffffffff is a NaN */
+    hip_ok(hipMemset(a_full, 0x5a, rows * d * 2), "sentinel");
+    check(fb_step(&sd, q, k, v, kb, vb, mask1, cache_a, cache_l, a_full, l_full, ws, ws_bytes, NULL, NULL) ==
+              FB_ERR_CACHE_INVALID, "reusing a never-written cache is refused (FB_FLAG_CHECK_CACHE)");
+    download(g_a, a_full, rows * d * 2);
+    int untouched = 1;
+    for (size_t i = 0; i < rows * d; ++i) untouched &= g_a[i] == 0x5a5a;
+    check(untouched, "nothing was written");
+    check(fb_step(&sd, q, k, v, kb, vb, mask0, cache_a, cache_l, a_full, l_full, ws, ws_bytes, NULL, NULL) == FB_OK,
+          "recomputing every head runs with the check on");
+    hip_ok(hipDeviceSynchronize(), "checked step");
+    download(g_a, a_full, rows * d * 2);
+    check(memcmp(g_a, f_a, rows * d * 2) == 0, "the checked step gives the fresh step's A_full bit for bit");
   }
 
   void* bufs[] = {q, k, v, kb, vb, dcu, cache_a, cache_l, a_full, l_full, a_out, l_out, a_in, l_in, a_m, l_m, ws,
