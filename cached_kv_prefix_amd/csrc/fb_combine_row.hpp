@@ -138,10 +138,11 @@ __device__ __forceinline__ int n_chunks(int n_keys, int chunk) { return (n_keys 
 
 // State of one output row between issuing its loads and finishing it.  A wave handles
 // one row at a time; the row index is wave-uniform, so the reuse inputs (flag, sequence
-// length, active list) are scalar loads, which do not wait behind vector loads, and every
-// partial load of the row (prefix, block, cached row) is issued before the reuse
-// decision is known.  Issuing several rows before finishing any keeps their round trips
-// in flight together.
+// length, active list) are scalar loads, which do not wait behind vector loads.  By
+// default every partial load of the row (prefix, block, cached row) is issued before the
+// reuse decision is known; with DECIDE (large launches, bound by bytes) the decision comes
+// first and only the loads the row uses are issued.  Issuing several rows before
+// finishing any keeps their round trips in flight together.
 template <int E, int UP, int UB>
 struct RowState {
   RowPartials<E, UP> PP;
