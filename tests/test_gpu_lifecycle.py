@@ -210,6 +210,36 @@ def test_block_run_similarity_large_block(gpu_lib):
     assert np.max(np.abs(got["ca"] - outs[1]) / (1.0 + np.abs(outs[1]))) <= 1e-5
 
 
+def test_block_run_large_block_matches_single_steps(gpu_lib):
+    """Block 2100 with 8 heads, three steps under the per-head rule: from step 2 half of the
+    heads reuse, and the combine (past the size where each row reads its decision before
+    its loads) also writes the cosine sums.  Every step's A_full, L_full and the final
+    cache equal, bit for bit, fb_step calls fed the masks the block run recorded."""
+    import torch
+    fb = gpu_lib
+    p = synth.custom(63, 1, 8, 2, 128, 2100, [1500], std=1.0)
+    dev = to_device(p)
+    s = _shape(fb, p, dev, False)
+    S = 3
+    q, kb, vb = _step_inputs(p, S, 64, [1e-3, 1.0] * 4)
+    plan = fb.BlockPlan(S, fb.FB_RULE_SIMILARITY, 0, 0.95)
+    say("[block] similarity, block 2100, three steps")
+    got = _run_block(fb, s, plan, dev, q, kb, vb, None, dev["k"], dev["v"])
+    assert got["masks"][2, 0, ::2].all() and not got["masks"][2, 0, 1::2].any(), got["masks"][2]
+    ca = torch.zeros(p.q.shape, device="cuda")
+    cl = torch.zeros(p.q.shape[:3], device="cuda")
+    af = torch.zeros(p.q.shape, dtype=torch.bfloat16, device="cuda")
+    lf = torch.zeros(p.q.shape[:3], device="cuda")
+    ws = torch.empty(max(fb.workspace_size(s), 16), dtype=torch.uint8, device="cuda")
+    for t in range(S):
+        m = None if t < 2 else torch.from_numpy(np.ascontiguousarray(got["masks"][t])).cuda()
+        fb.step(s, tensor(q[t]), dev["k"], dev["v"], tensor(kb[t]), tensor(vb[t]), m, ca, cl, af, lf, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(np_of(af).view(np.uint32), got["af"][t].view(np.uint32)), f"A_full step {t}"
+        assert np.array_equal(np_of(lf), got["lf"][t]), f"L_full step {t}"
+    assert np.array_equal(np_of(ca), got["ca"]) and np.array_equal(np_of(cl), got["cl"])
+
+
 def test_three_blocks(gpu_lib):
     """A multi-block run: the steps of a block under the threshold rule, then the block's
     last K/V appended to the prefix, three times; each block against the oracle chain."""
