@@ -217,7 +217,7 @@ __device__ __forceinline__ void row_issue(const CombineArgs& C, int rowid, int l
       const int dd = lane + 64 * e;
       st.cached[e] = dd < d ? C.cache_a[st.roff + dd] : 0.f;
     }
-    st.cached_l = C.cache_l[rowid];
+    st.cached_l = C.cache_l[st.rowid];   // the same (packed) row index as every other cache access
   }
   if constexpr (!DECIDE) read_reuse();
   st.nk = C.n_uniform;

@@ -175,8 +175,8 @@ __global__ void __launch_bounds__(256, FB_STREAM_WG_PER_CU) attn_stream_kernel(c
       bool okv_;                                                                              \
       const int tv_ = tok_of(kb_ + 4 * u + v_row, p0_, pv_, okv_);                            \
       const int off_ = ((tv_ - tok_base) * (int)tstride + (lane & 15) * 8) * 2;               \
-      kreg[SLOT][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off_, 0, 0)); \
-      vreg[SLOT][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off_, 0, 0)); \
+      kreg[SLOT][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, off_, 0, kKvLoadPolicy)); \
+      vreg[SLOT][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off_, 0, kKvLoadPolicy)); \
     }                                                                                         \
   } while (0)
 
