@@ -52,12 +52,13 @@ def block_run(q_steps, k, v, cu, kb_steps, vb_steps, scale: float, rule: str, m_
     """All steps of one block.  q_steps [S, b, B, H_q, d]; kb_steps, vb_steps [S, b, B, H_kv, d];
     rule "threshold" (m_steps [S, b], tau) or "similarity" (gamma).
     Returns dict(a_full [S,...], l_full [S,...], masks [S, b, H_q], sims [S, b, H_q] (nan
-    where not defined), cache_a, cache_l (after the last step))."""
+    where not defined), caches_a [S, b, B, H_q, d] and caches_l [S, b, B, H_q] (the cache
+    after each step), cache_a, cache_l (after the last step))."""
     S, b, B, h_q, d = np.asarray(q_steps).shape
     cache_a = np.zeros((b, B, h_q, d))
     cache_l = np.full((b, B, h_q), -np.inf)
     sim = None
-    out = dict(a_full=[], l_full=[], masks=[], sims=[])
+    out = dict(a_full=[], l_full=[], masks=[], sims=[], caches_a=[], caches_l=[])
     for s in range(S):
         if rule == "threshold":
             mask = np.zeros((b, h_q), np.uint8) if s == 0 else F.mask_threshold(m_steps[s], tau, h_q)
@@ -71,6 +72,8 @@ def block_run(q_steps, k, v, cu, kb_steps, vb_steps, scale: float, rule: str, m_
         out["l_full"].append(l)
         out["masks"].append(mask)
         out["sims"].append(sim)
+        out["caches_a"].append(new_a)
+        out["caches_l"].append(new_l)
         cache_a, cache_l = new_a, new_l
     res = {key: np.stack(val) for key, val in out.items()}
     res["cache_a"], res["cache_l"] = cache_a, cache_l

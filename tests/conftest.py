@@ -21,3 +21,13 @@ def gpu_lib():
     import cached_kv_prefix_amd as fb
     fb.load()          # raises if the shared library is missing: no silent fallback
     return fb
+
+
+@pytest.fixture(autouse=True)
+def _guard_bands():
+    """Checks, after each test, the canary regions around the buffers the test cut out with
+    tests.gpu_util.guarded (a no-op for tests that use none)."""
+    from tests import gpu_util
+    gpu_util.GUARDS.clear()
+    yield
+    gpu_util.check_guards()

@@ -6,20 +6,21 @@ import synth
 from synth.device import tensor, to_device
 from oracle.attention import attend, block_attention, lse_merge, prefix_attention, full_attention
 from oracle import flashblock as OF
-from tests.gpu_util import check_attn, check_lse, np_of, say
+from tests.gpu_util import check_attn, check_lse, guarded, np_of, say, to_device_guarded
 
 pytestmark = pytest.mark.gpu
 
 
 def _alloc(fb, p, dev):
+    """Step outputs, each between guard bands (checked after the test)."""
     import torch
     b, B, h, d = p.q.shape
     out_dt = torch.bfloat16 if p.dtype == "bf16" else torch.float32
     return dict(
-        cache_a=torch.zeros((b, B, h, d), dtype=torch.float32, device="cuda"),
-        cache_l=torch.zeros((b, B, h), dtype=torch.float32, device="cuda"),
-        a_full=torch.zeros((b, B, h, d), dtype=out_dt, device="cuda"),
-        l_full=torch.zeros((b, B, h), dtype=torch.float32, device="cuda"),
+        cache_a=guarded((b, B, h, d), torch.float32, 0.0, "cache_a"),
+        cache_l=guarded((b, B, h), torch.float32, 0.0, "cache_l"),
+        a_full=guarded((b, B, h, d), out_dt, 0.0, "a_full"),
+        l_full=guarded((b, B, h), torch.float32, 0.0, "l_full"),
     )
 
 
@@ -36,7 +37,7 @@ def _shape(fb, p, dev, varlen=False, num_splits=0):
 def _ws(fb, shape):
     import torch
     n = fb.workspace_size(shape)
-    return torch.full((max(n, 16),), 0xFF, dtype=torch.uint8, device="cuda")   # poisoned
+    return guarded((max(n, 16),), torch.uint8, 0xFF, "workspace")   # poisoned, between guard bands
 
 
 # ------------------------------------------------------------------------------ merge
@@ -53,8 +54,8 @@ def test_lse_merge_f32(gpu_lib, rows, d):
     li[::13] = lo[::13]
     lo[3] = li[3] = -np.inf
     t = lambda x: torch.from_numpy(x).cuda()
-    af = torch.empty((rows, d), dtype=torch.float32, device="cuda")
-    lf = torch.empty((rows,), dtype=torch.float32, device="cuda")
+    af = guarded((rows, d), torch.float32, name="a_full")
+    lf = guarded((rows,), torch.float32, name="l_full")
     fb.lse_merge(t(ao), t(lo), t(ai), t(li), af, lf)
     torch.cuda.synchronize()
     ea, el = lse_merge(ao, lo, ai, li)
@@ -63,7 +64,7 @@ def test_lse_merge_f32(gpu_lib, rows, d):
     check = np.isneginf(el)
     assert (np.isneginf(np_of(lf)) == check).all()
     assert (np.abs(np_of(lf)[~check] - el[~check]) <= 1e-6 * (1 + np.abs(el[~check]))).all()
-    afb = torch.empty((rows, d), dtype=torch.bfloat16, device="cuda")
+    afb = guarded((rows, d), torch.bfloat16, name="a_full bf16")
     fb.lse_merge(t(ao), t(lo), t(ai), t(li), afb)
     torch.cuda.synchronize()
     assert np.allclose(np_of(afb), ea, rtol=1e-2, atol=1e-2)
@@ -101,11 +102,11 @@ def test_prefix_and_block_attn(gpu_lib, case):
     name, b, hq, hkv, d, B, lens, dt = case
     say(f"[prefix/block] {name}")
     p = synth.custom(7, b, hq, hkv, d, B, lens, dtype=dt, std=1.0)
-    dev = to_device(p)
+    dev = to_device_guarded(p)
     shape = _shape(fb, p, dev, varlen=True)
     ws = _ws(fb, shape)
-    a = torch.full((b, B, hq, d), float("nan"), device="cuda")
-    l = torch.full((b, B, hq), float("nan"), device="cuda")
+    a = guarded((b, B, hq, d), torch.float32, float("nan"), "a_out")
+    l = guarded((b, B, hq), torch.float32, float("nan"), "l_out")
     fb.prefix_attn(shape, dev["q"], dev["k"], dev["v"], a, l, ws)
     torch.cuda.synchronize()
     ea, el = prefix_attention(p.q, p.k, p.v, p.cu, hkv, p.scale)
@@ -125,11 +126,11 @@ def test_prefix_peaked_softmax(gpu_lib):
     fb = gpu_lib
     p = synth.custom(11, 1, 4, 2, 128, 32, [3000], std=1.0)
     p.q *= 4.0   # sharper (values stay bf16: scaling by a power of two is exact)
-    dev = to_device(p)
+    dev = to_device_guarded(p)
     shape = _shape(fb, p, dev)
     ws = _ws(fb, shape)
-    a = torch.empty((1, 32, 4, 128), device="cuda")
-    l = torch.empty((1, 32, 4), device="cuda")
+    a = guarded((1, 32, 4, 128), torch.float32, name="a_out")
+    l = guarded((1, 32, 4), torch.float32, name="l_out")
     fb.prefix_attn(shape, dev["q"], dev["k"], dev["v"], a, l, ws)
     torch.cuda.synchronize()
     ea, el = prefix_attention(p.q, p.k, p.v, p.cu, 2, p.scale)
@@ -145,14 +146,14 @@ def test_split_counts_agree(gpu_lib, dt):
     import torch
     fb = gpu_lib
     p = synth.custom(3, 1, 4, 4, 128, 32, [4096], dtype=dt, std=1.0)
-    dev = to_device(p)
+    dev = to_device_guarded(p)
     ea, el = prefix_attention(p.q, p.k, p.v, p.cu, 4, p.scale)
     outs = []
     for ns in (1, 4, 32):
         shape = _shape(fb, p, dev, num_splits=ns)
         ws = _ws(fb, shape)
-        a = torch.empty((1, 32, 4, 128), device="cuda")
-        l = torch.empty((1, 32, 4), device="cuda")
+        a = guarded((1, 32, 4, 128), torch.float32, name=f"a_out splits {ns}")
+        l = guarded((1, 32, 4), torch.float32, name=f"l_out splits {ns}")
         fb.prefix_attn(shape, dev["q"], dev["k"], dev["v"], a, l, ws)
         torch.cuda.synchronize()
         outs.append((np_of(a), np_of(l)))
@@ -172,7 +173,7 @@ def test_tiny_f32_two_steps(gpu_lib):
     import torch
     fb = gpu_lib
     p = synth.tiny()
-    dev = to_device(p)
+    dev = to_device_guarded(p)
     shape = _shape(fb, p, dev)
     ws = _ws(fb, shape)
     o = _alloc(fb, p, dev)
@@ -207,7 +208,7 @@ def test_reuse_equals_recompute_bitwise(gpu_lib, block):
     fb = gpu_lib
     say(f"[reuse bitwise] block {block}")
     p = synth.custom(5, 2, 8, 2, 128, block, [2000, 777])
-    dev = to_device(p)
+    dev = to_device_guarded(p)
     shape = _shape(fb, p, dev, varlen=True)
     ws = _ws(fb, shape)
     o = _alloc(fb, p, dev)
@@ -239,13 +240,78 @@ def test_reuse_equals_recompute_bitwise(gpu_lib, block):
         assert torch.equal(x, y)
 
 
+MIXED_GROUP = [
+    # name, h_q, h_kv, B, prefix lengths: G * B rows per (sequence, KV head) group
+    ("streaming_rows32", 8, 2, 8, [900, 333]),        # 32 rows: streaming kernel
+    ("tiled_rows64", 8, 2, 16, [700, 1500]),          # 64 rows: query-tiled, 4 waves
+    ("wide_rows1200", 4, 1, 300, [640, 1100]),        # 1200 rows: query-tiled, 8 waves
+]
+
+
+@pytest.mark.parametrize("case", MIXED_GROUP, ids=[c[0] for c in MIXED_GROUP])
+def test_mixed_reuse_inside_gqa_group(gpu_lib, case):
+    """Each KV-head group holds both reusing and recomputing query heads, and the second
+    step changes the queries and the block K/V.  Against the oracle chain (fresh step, then
+    the mixed step on the oracle's own cache); the reused heads' cache rows must stay bit
+    for bit what the first step wrote, the recomputed heads' rows must take the new prefix
+    result."""
+    import torch
+    fb = gpu_lib
+    name, hq, hkv, B, lens = case
+    say(f"[mixed group] {name}")
+    p = synth.custom(81, 2, hq, hkv, 128, B, lens, std=1.0)
+    dev = to_device_guarded(p)
+    shape = _shape(fb, p, dev, varlen=True)
+    ws = _ws(fb, shape)
+    o = _alloc(fb, p, dev)
+    z = np.zeros((2, hq), np.uint8)
+    fb.step(shape, dev["q"], dev["k"], dev["v"], dev["k_blk"], dev["v_blk"], torch.from_numpy(z).cuda(),
+            o["cache_a"], o["cache_l"], o["a_full"], o["l_full"], ws)
+    torch.cuda.synchronize()
+    ea, el, ca, cl = OF.step(p.q, p.k, p.v, p.cu, p.k_blk, p.v_blk, z, None, None, p.scale)
+    check_attn(np_of(o["a_full"]), ea, "bf16", f"{name} fresh A_full")
+    check_attn(np_of(o["cache_a"]), ca, "bf16", f"{name} fresh cache")
+    ga0, gl0 = np_of(o["cache_a"]).copy(), np_of(o["cache_l"]).copy()
+    # every group mixes: sequence 0 reuses heads 1, 2 of each group of G, sequence 1 the others
+    G = hq // hkv
+    mask = np.zeros((2, hq), np.uint8)
+    for h in range(hq):
+        j = h % G
+        mask[0, h] = 1 if j in (1, 2) else 0
+        mask[1, h] = 1 - mask[0, h]
+    for b in range(2):
+        for g in range(hkv):
+            grp = mask[b, g * G:(g + 1) * G]
+            assert grp.any() and not grp.all(), (b, g, grp)
+    g_ = synth.rng(82)
+    q2 = synth.round_bf16(p.q + 0.3 * g_.standard_normal(p.q.shape, dtype=np.float32))
+    kb2 = synth.round_bf16(p.k_blk + 0.3 * g_.standard_normal(p.k_blk.shape, dtype=np.float32))
+    vb2 = synth.round_bf16(p.v_blk + 0.3 * g_.standard_normal(p.v_blk.shape, dtype=np.float32))
+    fb.step(shape, tensor(q2), dev["k"], dev["v"], tensor(kb2), tensor(vb2), torch.from_numpy(mask).cuda(),
+            o["cache_a"], o["cache_l"], o["a_full"], o["l_full"], ws)
+    torch.cuda.synchronize()
+    ea2, el2, ca2, cl2 = OF.step(q2, p.k, p.v, p.cu, kb2, vb2, mask, ca, cl, p.scale)
+    check_attn(np_of(o["a_full"]), ea2, "bf16", f"{name} mixed A_full")
+    check_lse(np_of(o["l_full"]), el2, "bf16", f"{name} mixed L_full")
+    ga, gl = np_of(o["cache_a"]), np_of(o["cache_l"])
+    check_attn(ga, ca2, "bf16", f"{name} mixed cache A_out")
+    check_lse(gl, cl2, "bf16", f"{name} mixed cache L_out")
+    for b in range(2):
+        for h in range(hq):
+            if mask[b, h]:
+                assert np.array_equal(ga[b, :, h], ga0[b, :, h]) and np.array_equal(gl[b, :, h], gl0[b, :, h]), \
+                    f"{name}: reused head ({b}, {h}) cache changed"
+            else:
+                assert not np.array_equal(ga[b, :, h], ga0[b, :, h]), f"{name}: head ({b}, {h}) was not recomputed"
+
+
 def test_threshold_block_of_steps(gpu_lib):
     """A block of denoising steps at the dLLM shape (shorter prefix): threshold rule on the
     drawn M, queries and block K/V changing every step, compared step by step."""
     import torch
     fb = gpu_lib
     p = synth.dllm(n_prefix=4096)
-    dev = to_device(p)
+    dev = to_device_guarded(p)
     shape = _shape(fb, p, dev)
     ws = _ws(fb, shape)
     o = _alloc(fb, p, dev)
@@ -265,12 +331,12 @@ def test_threshold_block_of_steps(gpu_lib):
         say(f"  step {s}: reuse={int(em[0, 0])}")
         check_attn(np_of(o["a_full"]), ea, "bf16", f"step {s} A_full")
         check_lse(np_of(o["l_full"]), el, "bf16", f"step {s} L_full")
+        # the oracle carries its own cache from step to step (an all-oracle chain)
+        check_attn(np_of(o["cache_a"]), ca, "bf16", f"step {s} cache A_out")
+        check_lse(np_of(o["cache_l"]), cl, "bf16", f"step {s} cache L_out")
         # next step: a few block tokens change
         q = synth.round_bf16(q + 0.05 * g.standard_normal(q.shape, dtype=np.float32) / np.sqrt(128))
         kb = synth.round_bf16(kb + 0.05 * g.standard_normal(kb.shape, dtype=np.float32) / np.sqrt(128))
-        # the GPU cache must track the oracle's cache for the next comparison
-        ca = np_of(o["cache_a"]).astype(np.float64)
-        cl = np_of(o["cache_l"]).astype(np.float64)
 
 
 def test_dllm_full_size_fresh_step_sampled(gpu_lib):
@@ -279,7 +345,7 @@ def test_dllm_full_size_fresh_step_sampled(gpu_lib):
     import torch
     fb = gpu_lib
     p = synth.dllm()
-    dev = to_device(p)
+    dev = to_device_guarded(p)
     shape = _shape(fb, p, dev)
     ws = _ws(fb, shape)
     o = _alloc(fb, p, dev)
@@ -303,17 +369,17 @@ def test_masks_and_cosine(gpu_lib):
     import torch
     fb = gpu_lib
     m = np.array([3, 4, 5, 0, 8, 1], dtype=np.int32)
-    mask = torch.empty((6, 5), dtype=torch.uint8, device="cuda")
+    mask = guarded((6, 5), torch.uint8, name="threshold mask")
     fb.mask_threshold(torch.from_numpy(m).cuda(), 4, 5, mask)
     sim = np.array([[0.95, 0.9500001, 0.2, 1.0, -0.3, 0.96]], dtype=np.float32)
-    ms = torch.empty((1, 6), dtype=torch.uint8, device="cuda")
+    ms = guarded((1, 6), torch.uint8, name="similarity mask")
     fb.mask_similarity(torch.from_numpy(sim).cuda(), 0.95, ms)
     g = np.random.default_rng(0)
     a0 = g.normal(size=(2, 9, 3, 128)).astype(np.float32)
     a1 = (a0 + 0.3 * g.normal(size=a0.shape)).astype(np.float32)
     a1[1, :, 2] = -a0[1, :, 2]
     a1[0, :, 1] = 0.0
-    s = torch.empty((2, 3), dtype=torch.float32, device="cuda")
+    s = guarded((2, 3), torch.float32, name="cosine")
     fb.head_cosine(torch.from_numpy(a0).cuda(), torch.from_numpy(a1).cuda(), s)
     torch.cuda.synchronize()
     assert (np_of(mask) == OF.mask_threshold(m, 4, 5)).all()
@@ -331,7 +397,7 @@ def test_ragged_gqa_sampled(gpu_lib):
     import torch
     fb = gpu_lib
     p = synth.ragged()
-    dev = to_device(p)
+    dev = to_device_guarded(p)
     shape = _shape(fb, p, dev, varlen=True)
     ws = _ws(fb, shape)
     o = _alloc(fb, p, dev)
@@ -363,7 +429,7 @@ def test_video_block_sampled(gpu_lib):
     import torch
     fb = gpu_lib
     p = synth.video()
-    dev = to_device(p)
+    dev = to_device_guarded(p)
     shape = _shape(fb, p, dev)
     ws = _ws(fb, shape)
     o = _alloc(fb, p, dev)
@@ -393,7 +459,7 @@ def test_step_threshold_equals_mask_then_step(gpu_lib):
     import torch
     fb = gpu_lib
     p = synth.custom(8, 3, 8, 2, 128, 32, [900, 64, 2000])
-    dev = to_device(p)
+    dev = to_device_guarded(p)
     shape = _shape(fb, p, dev, varlen=True)
     ws = _ws(fb, shape)
     o1, o2 = _alloc(fb, p, dev), _alloc(fb, p, dev)
@@ -431,16 +497,16 @@ def test_step_at_the_longest_swept_prefix(gpu_lib):
     kb = device_normal(74, (1, B, H, d), std)
     vb = device_normal(75, (1, B, H, d), std)
     s = fb.make_shape(1, H, H, d, B, seqlen_k=n)
-    ws = torch.empty(fb.workspace_size(s), dtype=torch.uint8, device="cuda")
-    ca = torch.zeros((1, B, H, d), device="cuda")
-    cl = torch.zeros((1, B, H), device="cuda")
-    af = torch.zeros((1, B, H, d), dtype=torch.bfloat16, device="cuda")
-    lf = torch.zeros((1, B, H), device="cuda")
+    ws = guarded((fb.workspace_size(s),), torch.uint8, name="workspace")
+    ca = guarded((1, B, H, d), torch.float32, 0.0, "cache_a")
+    cl = guarded((1, B, H), torch.float32, 0.0, "cache_l")
+    af = guarded((1, B, H, d), torch.bfloat16, 0.0, "a_full")
+    lf = guarded((1, B, H), torch.float32, 0.0, "l_full")
     say("[longest prefix] fresh step")
     fb.step(s, q, k, v, kb, vb, None, ca, cl, af, lf, ws)
     q2 = q + device_normal(76, (1, B, H, d), 0.01)
-    af2 = torch.zeros_like(af)
-    lf2 = torch.zeros_like(lf)
+    af2 = guarded((1, B, H, d), torch.bfloat16, 0.0, "a_full reuse")
+    lf2 = guarded((1, B, H), torch.float32, 0.0, "l_full reuse")
     fb.step(s, q2, k, v, kb, vb, torch.ones((1, H), dtype=torch.uint8, device="cuda"), ca, cl, af2, lf2, ws)
     torch.cuda.synchronize()
     heads = [5, 30]
@@ -455,7 +521,5 @@ def test_step_at_the_longest_swept_prefix(gpu_lib):
     check_attn(np_of(af)[:, :, heads], ea, "bf16", "longest fresh A_full")
     check_lse(np_of(lf)[:, :, heads], el, "bf16", "longest fresh L_full")
     check_attn(np_of(ca)[:, :, heads], na, "bf16", "longest cache")
-    ea2, el2, _, _ = OF.step(q2h, kh, vh, cu, kbh, vbh, np.ones((1, 2), np.uint8),
-                             np_of(ca)[:, :, heads].astype(np.float64), np_of(cl)[:, :, heads].astype(np.float64),
-                             1.0 / np.sqrt(d))
+    ea2, el2, _, _ = OF.step(q2h, kh, vh, cu, kbh, vbh, np.ones((1, 2), np.uint8), na, nl, 1.0 / np.sqrt(d))
     check_attn(np_of(af2)[:, :, heads], ea2, "bf16", "longest reuse A_full")

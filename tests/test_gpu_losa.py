@@ -7,14 +7,14 @@ import synth
 from synth.device import tensor, to_device
 from oracle import losa as OL
 from oracle.attention import prefix_attention
-from tests.gpu_util import check_attn, check_lse, np_of, say
+from tests.gpu_util import check_attn, check_lse, guarded, guarded_copy, np_of, say, to_device_guarded
 
 pytestmark = pytest.mark.gpu
 
 
 def _setup(fb, p, q_cur, q_prev, n_active, page, topk):
     import torch
-    dev = to_device(p)
+    dev = to_device_guarded(p)
     code = fb.FB_BF16 if p.dtype == "bf16" else fb.FB_F32
     if p.batch == 1:
         s = fb.make_shape(p.batch, p.h_q, p.h_kv, p.d, p.B, dtype=code, seqlen_k=int(p.seqlens[0]))
@@ -24,18 +24,20 @@ def _setup(fb, p, q_cur, q_prev, n_active, page, topk):
     ls = fb.make_losa_shape(s, page_size=page, topk=topk, n_active=n_active)
     el = 2 if p.dtype == "bf16" else 4
     nb = fb.losa_meta_bytes(ls)
-    kmin = torch.empty(nb // el, dtype=dev["k"].dtype, device="cuda")
-    kmax = torch.empty(nb // el, dtype=dev["k"].dtype, device="cuda")
+    kmin = guarded((nb // el,), dev["k"].dtype, name="kmin")
+    kmax = guarded((nb // el,), dev["k"].dtype, name="kmax")
     fb.losa_page_meta(ls, dev["k"], kmin, kmax)
     cap = fb.losa_union_capacity(ls)
     out = dict(
-        active=torch.full((p.batch, n_active), -7, dtype=torch.int32, device="cuda"),
-        topk=torch.full((p.batch, p.h_q, n_active, topk), -7, dtype=torch.int32, device="cuda"),
-        union=torch.full((p.batch, p.h_kv, cap), -7, dtype=torch.int32, device="cuda"),
-        count=torch.full((p.batch, p.h_kv), -7, dtype=torch.int32, device="cuda"),
-        ws=torch.empty(fb.losa_workspace_size(ls), dtype=torch.uint8, device="cuda"),
+        active=guarded((p.batch, n_active), torch.int32, -7, "active"),
+        topk=guarded((p.batch, p.h_q, n_active, topk), torch.int32, -7, "topk_pages"),
+        union=guarded((p.batch, p.h_kv, cap), torch.int32, -7, "union_pages"),
+        count=guarded((p.batch, p.h_kv), torch.int32, -7, "union_count"),
+        ws=guarded((fb.losa_workspace_size(ls),), torch.uint8, name="losa workspace"),
     )
     dev.update(q_cur=tensor(q_cur, p.dtype), q_prev=tensor(q_prev, p.dtype), kmin=kmin, kmax=kmax)
+    for key in ("q_cur", "q_prev"):
+        dev[key] = guarded_copy(dev[key], key)
     return dev, s, ls, out
 
 
@@ -100,11 +102,11 @@ def test_select_union_and_step_small(gpu_lib, case):
     _check_selection(p, out, exp, nA)
 
     # full sparse step on top of a cache filled by a dense step on q_prev
-    ca = torch.zeros((b, B, hq, d), device="cuda")
-    cl = torch.zeros((b, B, hq), device="cuda")
-    a_full = torch.zeros((b, B, hq, d), dtype=dev["q"].dtype, device="cuda")
-    l_full = torch.zeros((b, B, hq), device="cuda")
-    ws = torch.empty(max(fb.workspace_size(s), 16), dtype=torch.uint8, device="cuda")
+    ca = guarded((b, B, hq, d), torch.float32, 0.0, "cache_a")
+    cl = guarded((b, B, hq), torch.float32, 0.0, "cache_l")
+    a_full = guarded((b, B, hq, d), dev["q"].dtype, 0.0, "a_full")
+    l_full = guarded((b, B, hq), torch.float32, 0.0, "l_full")
+    ws = guarded((max(fb.workspace_size(s), 16),), torch.uint8, name="step workspace")
     fb.step(s, dev["q_prev"], dev["k"], dev["v"], dev["k_blk"], dev["v_blk"], None, ca, cl, a_full, l_full, ws)
     torch.cuda.synchronize()
     cache0_a, cache0_l = np_of(ca).astype(np.float64), np_of(cl).astype(np.float64)
@@ -117,11 +119,12 @@ def test_select_union_and_step_small(gpu_lib, case):
                  out["ws"])
     torch.cuda.synchronize()
     _check_selection(p, out, exp, nA)
-    ea, el, na, nl, _ = OL.step(q_cur, q_prev, p.k, p.v, p.cu, p.k_blk, p.v_blk, cache0_a, cache0_l, nA, page,
-                                topk, p.scale)
+    # the oracle continues from its own dense cache (an all-oracle chain)
+    ea, el, na, nl, _ = OL.step(q_cur, q_prev, p.k, p.v, p.cu, p.k_blk, p.v_blk, ea0, el0, nA, page, topk, p.scale)
     check_attn(np_of(a_full), ea, dt, f"{name} A_full")
     check_lse(np_of(l_full), el, dt, f"{name} L_full")
     check_attn(np_of(ca), na, dt, f"{name} new cache")
+    check_lse(np_of(cl), nl, dt, f"{name} new cache L")
     stable = np.ones(B, bool)
     stable[exp["active"][0]] = False
     assert (np_of(ca)[0, stable] == cache0_a[0, stable]).all()
@@ -192,11 +195,11 @@ def test_losa_full_size(gpu_lib):
     q_cur, q_prev = p.extra["q_cur"], p.extra["q_prev"]
     dev, s, ls, out = _setup(fb, p, q_cur, q_prev, 8, 16, 64)
     say("[losa full] dense step 0")
-    ca = torch.zeros((1, 64, 32, 128), device="cuda")
-    cl = torch.zeros((1, 64, 32), device="cuda")
-    a_full = torch.zeros((1, 64, 32, 128), dtype=torch.bfloat16, device="cuda")
-    l_full = torch.zeros((1, 64, 32), device="cuda")
-    ws = torch.empty(fb.workspace_size(s), dtype=torch.uint8, device="cuda")
+    ca = guarded((1, 64, 32, 128), torch.float32, 0.0, "cache_a")
+    cl = guarded((1, 64, 32), torch.float32, 0.0, "cache_l")
+    a_full = guarded((1, 64, 32, 128), torch.bfloat16, 0.0, "a_full")
+    l_full = guarded((1, 64, 32), torch.float32, 0.0, "l_full")
+    ws = guarded((fb.workspace_size(s),), torch.uint8, name="step workspace")
     fb.step(s, dev["q_prev"], dev["k"], dev["v"], dev["k_blk"], dev["v_blk"], None, ca, cl, a_full, l_full, ws)
     torch.cuda.synchronize()
     cache0_a, cache0_l = np_of(ca).astype(np.float64), np_of(cl).astype(np.float64)
@@ -205,12 +208,17 @@ def test_losa_full_size(gpu_lib):
                  dev["kmax"], ca, cl, a_full, l_full, out["active"], out["topk"], out["union"], out["count"],
                  out["ws"])
     torch.cuda.synchronize()
-    say("[losa full] oracle")
-    ea, el, na, nl, sel = OL.step(q_cur, q_prev, p.k, p.v, p.cu, p.k_blk, p.v_blk, cache0_a, cache0_l, 8, 16, 64,
-                                  p.scale)
+    say("[losa full] oracle (dense step 0, then the sparse step on the oracle's own cache)")
+    ea0, el0 = prefix_attention(q_prev, p.k, p.v, p.cu, p.h_kv, p.scale)
+    check_attn(cache0_a, ea0, "bf16", "losa dense cache")
+    ea, el, na, nl, sel = OL.step(q_cur, q_prev, p.k, p.v, p.cu, p.k_blk, p.v_blk, ea0, el0, 8, 16, 64, p.scale)
     assert (sel["active"][0] == p.extra["moved"]).all()
     _check_selection(p, out, sel, 8)
     check_attn(np_of(a_full), ea, "bf16", "losa A_full")
     check_lse(np_of(l_full), el, "bf16", "losa L_full")
     check_attn(np_of(ca), na, "bf16", "losa cache")
+    check_lse(np_of(cl), nl, "bf16", "losa cache L")
+    stable = np.ones(64, bool)
+    stable[sel["active"][0]] = False
+    assert (np_of(ca)[0, stable] == cache0_a[0, stable]).all()
     say(f"[losa full] union pages per head: mean {np_of(out['count']).mean():.1f} of 8192")

@@ -6,13 +6,13 @@ import pytest
 import synth
 from synth.device import tensor, to_device
 from oracle import residual as OR
-from tests.gpu_util import check_attn, check_lse, np_of, say
+from tests.gpu_util import check_attn, check_lse, guarded, np_of, say, to_device_guarded
 
 pytestmark = pytest.mark.gpu
 
 
 def _shape(fb, p, page, max_sel):
-    dev = to_device(p)
+    dev = to_device_guarded(p)
     code = fb.FB_BF16 if p.dtype == "bf16" else fb.FB_F32
     if p.batch == 1:
         s = fb.make_shape(p.batch, p.h_q, p.h_kv, p.d, p.B, dtype=code, seqlen_k=int(p.seqlens[0]))
@@ -26,10 +26,11 @@ def _shape(fb, p, page, max_sel):
 def _bufs(fb, p, rs, dev):
     import torch
     b, B, hq, d = p.batch, p.B, p.h_q, p.d
-    return dict(ca=torch.full((b, B, hq, d), 7.0, device="cuda"), cl=torch.full((b, B, hq), 7.0, device="cuda"),
-                af=torch.zeros((b, B, hq, d), dtype=dev["q"].dtype, device="cuda"),
-                lf=torch.zeros((b, B, hq), device="cuda"),
-                ws=torch.empty(fb.residual_workspace_size(rs), dtype=torch.uint8, device="cuda"))
+    return dict(ca=guarded((b, B, hq, d), torch.float32, 7.0, "cache_a"),
+                cl=guarded((b, B, hq), torch.float32, 7.0, "cache_l"),
+                af=guarded((b, B, hq, d), dev["q"].dtype, 0.0, "a_full"),
+                lf=guarded((b, B, hq), torch.float32, 0.0, "l_full"),
+                ws=guarded((fb.residual_workspace_size(rs),), torch.uint8, name="workspace"))
 
 
 def _sel_dev(sel, max_sel, seed):
@@ -88,8 +89,11 @@ def test_residual_steps_small(gpu_lib, case):
     check_attn(np_of(bf["ca"]), na, dt, f"{name} refresh residual")
     check_lse(np_of(bf["cl"]), nl, dt, f"{name} refresh residual L")
 
-    # step 2: even heads reuse the GPU's cache; new queries and a new selection
+    # step 2: even heads reuse the cache; new queries and a new selection.  The oracle
+    # continues from its own step-1 cache (an all-oracle chain); the GPU's reused rows must
+    # stay bit for bit what the GPU wrote in step 1.
     cache1_a, cache1_l = np_of(bf["ca"]).astype(np.float64), np_of(bf["cl"]).astype(np.float64)
+    o1a, o1l = na, nl
     g = synth.rng(35)
     q2 = p.q + 0.1 * g.standard_normal(p.q.shape, dtype=np.float32)
     q2 = synth.round_bf16(q2) if dt == "bf16" else q2.astype(np.float32)
@@ -99,12 +103,13 @@ def test_residual_steps_small(gpu_lib, case):
     q2d = tensor(q2, dt)
     _run(fb, rs, q2d, dev, sp, sc, torch.from_numpy(mask).cuda(), bf)
     torch.cuda.synchronize()
-    ea, el, na, nl = OR.step(q2, p.k, p.v, p.cu, p.k_blk, p.v_blk, sel2, page, mask, cache1_a, cache1_l, p.scale)
+    ea, el, na, nl = OR.step(q2, p.k, p.v, p.cu, p.k_blk, p.v_blk, sel2, page, mask, o1a, o1l, p.scale)
     check_attn(np_of(bf["af"]), ea, dt, f"{name} mixed A_full")
     check_lse(np_of(bf["lf"]), el, dt, f"{name} mixed L_full")
     ga, gl = np_of(bf["ca"]), np_of(bf["cl"])
     assert (ga[:, :, ::2] == cache1_a[:, :, ::2]).all() and (gl[:, :, ::2] == cache1_l[:, :, ::2]).all()
     check_attn(ga, na, dt, f"{name} mixed residual")
+    check_lse(gl, nl, dt, f"{name} mixed residual L")
 
     # reuse with unchanged inputs and cache gives the refresh output bit for bit
     _run(fb, rs, q2d, dev, sp, sc, None, bf)
@@ -152,8 +157,7 @@ def test_residual_full_size(gpu_lib):
     check_attn(sub(af1), ea, "bf16", "full refresh A_full")
     check_lse(sub(lf1), el, "bf16", "full refresh L_full")
     check_attn(sub(cache_a), na, "bf16", "full residual")
-    ea, el, _, _ = OR.step(sub(q2), k, v, p.cu, kb, vb, hsel, page, np.ones((1, 3), np.uint8), sub(cache_a),
-                           sub(cache_l), p.scale)
+    ea, el, _, _ = OR.step(sub(q2), k, v, p.cu, kb, vb, hsel, page, np.ones((1, 3), np.uint8), na, nl, p.scale)
     check_attn(sub(af2), ea, "bf16", "full reuse A_full")
     check_lse(sub(lf2), el, "bf16", "full reuse L_full")
 

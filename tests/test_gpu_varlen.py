@@ -6,7 +6,7 @@ import pytest
 import synth
 from synth.device import tensor
 from oracle.varlen import prefix_attention_varlen
-from tests.gpu_util import check_attn, check_lse, np_of, say
+from tests.gpu_util import check_attn, check_lse, guarded, np_of, say
 
 pytestmark = pytest.mark.gpu
 
@@ -21,9 +21,9 @@ def _run(fb, br, b_max):
                       max_seqlen_k=int(br["seqlens"].max()))
     tq = int(br["cu_q"][-1])
     vs = fb.make_varlen_shape(s, cu_q, tq)
-    ws = torch.empty(fb.prefix_attn_varlen_workspace_size(vs), dtype=torch.uint8, device="cuda")
-    a = torch.full((tq, br["h_q"], br["d"]), float("nan"), device="cuda")
-    l = torch.full((tq, br["h_q"]), float("nan"), device="cuda")
+    ws = guarded((max(fb.prefix_attn_varlen_workspace_size(vs), 16),), torch.uint8, name="varlen workspace")
+    a = guarded((tq, br["h_q"], br["d"]), torch.float32, float("nan"), "a_out packed")
+    l = guarded((tq, br["h_q"]), torch.float32, float("nan"), "l_out packed")
     k = tensor(br["k"], br["dtype"]) if br["k"].shape[0] else None
     v = tensor(br["v"], br["dtype"]) if br["v"].shape[0] else None
     fb.prefix_attn_varlen(vs, tensor(br["q"], br["dtype"]), k, v, a, l, ws)
