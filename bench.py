@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--only-main", action="store_true", help="headline workload only (for profiling)")
     ap.add_argument("--only-others", action="store_true",
                     help="ragged-GQA and LoSA sparse steps only, one JSON line of their times (for profiling)")
+    ap.add_argument("--only-video", choices=["masked", "fresh"], default=None,
+                    help="video-block steps only, masked (7 of 12 heads reuse) or all fresh, one JSON line of "
+                         "their time (for profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (counter calibration)")
@@ -285,6 +288,61 @@ def cpu_baseline(p):
     return out
 
 
+def cpu_baseline_others(probs):
+    """The oracle (as it stands, all host BLAS threads) on bounded samples of the other
+    workloads' steps, each scaled to its whole step:
+      * video block, masked step (7 of 12 heads reuse): a seeded 256 of the 4680 block rows,
+        every head (recomputing heads: prefix + block + merge; reusing heads: block + merge
+        on stand-in cached rows), scaled by 4680 / 256;
+      * ragged GQA, all-fresh step: 2 of the 8 sequences, every head, scaled by the total
+        prefix length over theirs;
+      * LoSA sparse step: the whole step (selection, sparse prefix for the active rows,
+        block and merge for all 64 rows) on stand-in cached rows."""
+    import synth
+    from oracle import flashblock as OF
+    from oracle import losa as OL
+    out = {}
+    p = probs.get("video")
+    if p is not None:
+        rows = np.sort(synth.rng(31).choice(p.B, size=256, replace=False))
+        mask = OF.mask_similarity(p.extra["sim"], p.extra["gamma"])
+        ca = np.zeros((1, 256, p.h_q, p.d))
+        cl = np.zeros((1, 256, p.h_q))
+        t0 = time.perf_counter()
+        OF.step(p.q[:, rows], p.k, p.v, p.cu, p.k_blk, p.v_blk, mask, ca, cl, p.scale)
+        step_s = (time.perf_counter() - t0) * p.B / 256
+        n_fresh = int((mask == 0).sum())
+        flop = 4.0 * p.B * p.B * p.d * p.h_q + n_fresh * 4.0 * p.B * int(p.seqlens[0]) * p.d
+        out["video_block"] = dict(value=flop / step_s / 1e12, unit="TFLOP/s", step_ms=step_s * 1e3,
+                                  sample="masked step on 256 of 4680 block rows x 12 heads, scaled to 4680 rows")
+    p = probs.get("ragged")
+    if p is not None:
+        t0 = time.perf_counter()
+        n_s = 0
+        for b in (0, 1):
+            lo, hi = int(p.cu[b]), int(p.cu[b + 1])
+            z = np.zeros((1, p.h_q), np.uint8)
+            OF.step(p.q[b:b + 1], p.k[lo:hi], p.v[lo:hi], np.array([0, hi - lo], np.int32), p.k_blk[b:b + 1],
+                    p.v_blk[b:b + 1], z, None, None, p.scale)
+            n_s += hi - lo
+        step_s = (time.perf_counter() - t0) * float(p.seqlens.sum()) / n_s
+        kv = float(p.seqlens.sum()) * p.h_kv * p.d * 4
+        out["ragged_gqa"] = dict(value=kv / step_s / 1e9, unit="GB/s", step_ms=step_s * 1e3,
+                                 sample=f"all-fresh step of sequences 0 and 1 ({n_s} of {int(p.seqlens.sum())} "
+                                        f"prefix tokens), scaled to the 8 sequences")
+    p = probs.get("losa")
+    if p is not None:
+        ca = np.zeros(p.q.shape)
+        cl = np.zeros(p.q.shape[:3])
+        t0 = time.perf_counter()
+        OL.step(p.extra["q_cur"], p.extra["q_prev"], p.k, p.v, p.cu, p.k_blk, p.v_blk, ca, cl, 8, 16, 64, p.scale)
+        step_s = time.perf_counter() - t0
+        out["losa_sparse"] = dict(value=step_s * 1e3, unit="ms per sparse step", step_ms=step_s * 1e3,
+                                  sample="the whole sparse step (131072-token prefix, 32 heads, B 64, |A| 8, "
+                                         "top-64 of 8192 pages)")
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -307,6 +365,9 @@ def main():
     if args.only_others:
         print(json.dumps({"only_others": only_others(fb, args)}))
         return
+    if args.only_video:
+        print(json.dumps({"only_video": only_video(fb, args, args.only_video)}))
+        return
 
     # ---------------------------------------------------------------- headline workload
     p = synth.dllm()
@@ -328,6 +389,7 @@ def main():
              "attn_kernel_us_p10_p50_p90": [float(x) for x in kq], "tokens_per_s": p.B / wall,
              "kv_bytes": kv_bytes, "attn_kernel_alg_bytes": attn_bytes,
              "step_frac_of_hbm_peak": value / HBM_PEAK_GBS}
+    problems = {}
     if not args.only_main:
         # reuse step: every head reuses, only the block pass and the merge run
         one = torch.zeros_like(m_fresh)
@@ -350,7 +412,7 @@ def main():
         extra["cold_fresh_step_us_p10_p50_p90"] = [float(x) for x in np.percentile(cold, [10, 50, 90])]
         ceil = measured_ceilings(kv_bytes)
         extra["ceilings"] = ceil
-        extra["workloads"] = other_workloads(fb, args)
+        extra["workloads"] = other_workloads(fb, args, keep=problems)
         vb = extra["workloads"]["video_block"]
         vb["masked_frac_of_measured_mfma"] = vb["masked_TFLOPs"] / ceil["mfma_bf16_TFLOPs"]
         vb["attn_kernel_all_fresh_frac_of_measured_mfma"] = (vb["attn_kernel_all_fresh_frac_mfma"] * MFMA_BF16_PEAK_TFLOPS
@@ -375,6 +437,8 @@ def main():
         result["roofline"]["frac_of_measured"] = achieved / extra["ceilings"]["stream_read_GBps"]
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(p)
+        if problems:
+            result["cpu_baseline"]["other_workloads"] = cpu_baseline_others(problems)
     print(json.dumps(result))
 
 
@@ -466,11 +530,13 @@ def context_sweep(fb, args, lengths=(102400, 204800, 409600, 819200)):
 def lifecycle_workload(fb, args, blocks=4, S=8):
     """Multi-block run on the dLLM step shape (32 heads, d 128, B 32): a prefix of 32768
     tokens grows by one block per block.  Per block: fb_block_run over S steps under the
-    threshold rule (tau 4; M drawn as in the dLLM workload, one draw per block), then
+    threshold rule (tau 4; M drawn as in the dLLM workload, one draw per block), the same
+    steps under the per-head similarity rule (gamma 0.95: a head reuses from step 2 on when
+    the cosine of its cached A_out before and after the previous step is above gamma), then
     fb_append_block in place.  Per-step queries drift by N(0, 0.01^2) around the block's
     queries and the block K/V by N(0, 0.05^2); inputs are drawn on the device from a seeded
-    generator.  Reports the time per block and per step, and the reuse statistics (the
-    masks each step used, and the per-head cosine of consecutive prefix outputs)."""
+    generator.  Reports the time per block and per step, and the reuse statistics of each
+    rule (the masks each step used, and the per-head cosine of consecutive prefix outputs)."""
     import torch
     gen = torch.Generator(device="cuda")
     gen.manual_seed(13)
@@ -485,8 +551,9 @@ def lifecycle_workload(fb, args, blocks=4, S=8):
     v = torch.empty_like(k)
     k[:N0] = draw(N0, H, d)
     v[:N0] = draw(N0, H, d)
-    plan = fb.BlockPlan(S, fb.FB_RULE_THRESHOLD, 4, 0.0)
-    per_block = []
+    plans = {"threshold": fb.BlockPlan(S, fb.FB_RULE_THRESHOLD, 4, 0.0),
+             "similarity": fb.BlockPlan(S, fb.FB_RULE_SIMILARITY, 0, 0.95)}
+    per_rule = {r: [] for r in plans}
     for j in range(blocks):
         q0, kb0, vb0 = draw(1, B, H, d), draw(1, B, H, d), draw(1, B, H, d)
         q = torch.stack([q0 + draw(1, B, H, d, std=0.01) for _ in range(S)])
@@ -494,29 +561,35 @@ def lifecycle_workload(fb, args, blocks=4, S=8):
         vb = torch.stack([vb0 + draw(1, B, H, d, std=0.05) for _ in range(S)])
         n = N0 + j * B
         shape = fb.make_shape(1, H, H, d, B, seqlen_k=n)
-        bufs = dict(ca=torch.zeros((1, B, H, d), device="cuda"), cl=torch.zeros((1, B, H), device="cuda"),
-                    af=torch.empty((S, 1, B, H, d), dtype=torch.bfloat16, device="cuda"),
-                    masks=torch.empty((S, 1, H), dtype=torch.uint8, device="cuda"),
-                    sims=torch.empty((S, 1, H), device="cuda"),
-                    ws=torch.empty(fb.block_workspace_size(shape), dtype=torch.uint8, device="cuda"))
         m = torch.from_numpy(m_all[j]).cuda()
+        for rule, plan in plans.items():
+            bufs = dict(ca=torch.zeros((1, B, H, d), device="cuda"), cl=torch.zeros((1, B, H), device="cuda"),
+                        af=torch.empty((S, 1, B, H, d), dtype=torch.bfloat16, device="cuda"),
+                        masks=torch.empty((S, 1, H), dtype=torch.uint8, device="cuda"),
+                        sims=torch.empty((S, 1, H), device="cuda"),
+                        ws=torch.empty(fb.block_workspace_size(shape), dtype=torch.uint8, device="cuda"))
 
-        def run(tr):
-            fb.block_run(shape, plan, q, k, v, kb, vb, m, bufs["ca"], bufs["cl"], bufs["af"], None, bufs["masks"],
-                         bufs["sims"], bufs["ws"])
-        wall = wall_time(run, max(3, args.steps // 10), 1)
+            def run(tr):
+                fb.block_run(shape, plan, q, k, v, kb, vb, m if rule == "threshold" else None, bufs["ca"],
+                             bufs["cl"], bufs["af"], None, bufs["masks"], bufs["sims"], bufs["ws"])
+            wall = wall_time(run, max(3, args.steps // 10), 1)
+            masks = bufs["masks"].cpu().numpy()
+            sims = bufs["sims"].cpu().numpy()[1:]
+            per_rule[rule].append({"prefix": n, "block_us": wall * 1e6, "step_mean_us": wall / S * 1e6,
+                                   "reused_head_steps": int(masks.sum()), "head_steps": int(masks.size),
+                                   "sim_min": float(np.nanmin(sims)), "sim_mean": float(np.nanmean(sims))})
         fb.append_block(shape, k, v, kb[-1], vb[-1], k, v)   # in place: the block follows the prefix
-        masks = bufs["masks"].cpu().numpy()
-        sims = bufs["sims"].cpu().numpy()[1:]
-        per_block.append({"prefix": n, "block_us": wall * 1e6, "step_mean_us": wall / S * 1e6,
-                          "reused_head_steps": int(masks.sum()), "head_steps": int(masks.size),
-                          "sim_min": float(np.nanmin(sims)), "sim_mean": float(np.nanmean(sims))})
     torch.cuda.synchronize()
-    reused = sum(b_["reused_head_steps"] for b_ in per_block)
-    total = sum(b_["head_steps"] for b_ in per_block)
-    return {"blocks": per_block, "reuse_fraction": reused / total,
-            "step_mean_us": float(np.mean([b_["step_mean_us"] for b_ in per_block])),
-            "prefix_final": N0 + blocks * B}
+    out = {"prefix_final": N0 + blocks * B}
+    for rule, per_block in per_rule.items():
+        reused = sum(b_["reused_head_steps"] for b_ in per_block)
+        total = sum(b_["head_steps"] for b_ in per_block)
+        out[rule] = {"blocks": per_block, "reuse_fraction": reused / total,
+                     "step_mean_us": float(np.mean([b_["step_mean_us"] for b_ in per_block]))}
+    # the threshold rule's figures at the top level, as before
+    out["reuse_fraction"] = out["threshold"]["reuse_fraction"]
+    out["step_mean_us"] = out["threshold"]["step_mean_us"]
+    return out
 
 
 def varlen_workload(fb, args):
@@ -545,14 +618,18 @@ def varlen_workload(fb, args):
             "branches": len(blocks), "query_rows": tq, "block_sizes": blocks}
 
 
-def other_workloads(fb, args):
+def other_workloads(fb, args, keep=None):
+    """The workloads beside the headline one; `keep` (a dict) receives their host problems,
+    which the CPU baseline times the oracle on."""
     import torch
     import synth
     from synth.device import to_device, tensor
     out = {}
+    keep = {} if keep is None else keep
     steps = max(5, args.steps // 5)
     # ragged GQA: per-sequence threshold mask from the drawn M
     p = synth.ragged()
+    keep["ragged"] = p
     dev = to_device(p)
     shape, bufs = setup_step(fb, p, dev, varlen=True)
     fresh = torch.full((p.batch,), 1 << 30, dtype=torch.int32, device="cuda")
@@ -561,12 +638,18 @@ def other_workloads(fb, args):
     w_m, _, _ = time_steps(lambda tr: run_step(fb, shape, dev, bufs, m, trace=tr), steps, 3)
     kv = int(p.seqlens.sum()) * p.h_kv * p.d * 4
     fresh_frac = float((p.extra["m_updated"] >= 4).mean())
-    out["ragged_gqa"] = {"fresh_step_us": w_f * 1e6, "attn_kernel_us": a_f * 1e6, "kv_GBps": kv / w_f / 1e9,
-                         "frac_hbm": kv / a_f / 1e9 / HBM_PEAK_GBS, "masked_step_us": w_m * 1e6,
+    # The event pair around the attention launch is recorded in a second pass and also spans
+    # the launch gap; a kernel time above the step's own wall time is not credible, so the
+    # kernel fraction uses the smaller of the two (rocprofv3 durations are in profiles/).
+    a_k = min(a_f, w_f)
+    out["ragged_gqa"] = {"fresh_step_us": w_f * 1e6, "attn_kernel_us_events": a_f * 1e6, "attn_kernel_us": a_k * 1e6,
+                         "kv_GBps": kv / w_f / 1e9, "frac_hbm_step": kv / w_f / 1e9 / HBM_PEAK_GBS,
+                         "frac_hbm": kv / a_k / 1e9 / HBM_PEAK_GBS, "masked_step_us": w_m * 1e6,
                          "fresh_sequences": fresh_frac, "total_prefix_tokens": int(p.seqlens.sum())}
     del dev, bufs
     # video block: per-head similarity mask, 7 of 12 heads reuse
     p = synth.video()
+    keep["video"] = p
     dev = to_device(p)
     shape, bufs = setup_step(fb, p, dev)
     sim = torch.from_numpy(p.extra["sim"]).cuda()
@@ -578,14 +661,19 @@ def other_workloads(fb, args):
     n_fresh = int((p.extra["sim"] <= np.float32(p.extra["gamma"])).sum())
     f_masked = flop_block + n_fresh * flop_pre
     f_all = flop_block + p.h_q * flop_pre
+    a_all, a_m = min(a_all, w_all), min(a_m, w_m)   # event pairs include the launch gap; see ragged_gqa
     out["video_block"] = {"masked_step_us": w_m * 1e6, "masked_TFLOPs": f_masked / w_m / 1e12,
                           "masked_frac_mfma": f_masked / w_m / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                          "masked_attn_kernel_us": a_m * 1e6,
+                          "masked_attn_kernel_frac_mfma": f_masked / a_m / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                           "all_fresh_step_us": w_all * 1e6, "all_fresh_TFLOPs": f_all / w_all / 1e12,
+                          "attn_kernel_all_fresh_us": a_all * 1e6,
                           "attn_kernel_all_fresh_frac_mfma": f_all / a_all / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                           "fresh_heads": n_fresh, "tokens_per_s": nq / w_m}
     del dev, bufs
     # LoSA sparse step
     p, dev, shape, bufs, ls, sparse, sel, cap = losa_setup(fb)
+    keep["losa"] = p
     fresh = torch.full((1,), 1 << 30, dtype=torch.int32, device="cuda")
     w_d, _, _ = time_steps(lambda tr: run_step(fb, shape, dev, bufs, fresh, trace=tr), steps, 2)
     # a short step (about 0.1 ms): the full step count and more warm-up, as for the dLLM steps
@@ -647,6 +735,20 @@ def only_others(fb, args):
     w_s = wall_time(sparse, args.steps, args.warmup)
     return {"ragged_fresh_step_us": w_r * 1e6, "losa_sparse_step_us": w_s * 1e6,
             "union_pages": int(sel["count"].sum().item())}
+
+
+def only_video(fb, args, which):
+    """Profiling mode: `steps` video-block steps after `warmup`, either masked (the per-head
+    similarity rule with the drawn similarities: 7 of 12 heads reuse) or all fresh."""
+    import torch
+    import synth
+    from synth.device import to_device
+    p = synth.video()
+    dev = to_device(p)
+    shape, bufs = setup_step(fb, p, dev)
+    sim = torch.from_numpy(p.extra["sim"]).cuda() if which == "masked" else None
+    w = wall_time(lambda tr: run_step(fb, shape, dev, bufs, None, sim=sim), args.steps, args.warmup)
+    return {"which": which, "step_us": w * 1e6}
 
 
 def residual_workload(fb, p, dev, shape, sel, cap, steps, short_steps):
