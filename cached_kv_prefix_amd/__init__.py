@@ -18,7 +18,7 @@ STATUS = {0: "FB_OK", 1: "FB_ERR_INVALID_ARG", 2: "FB_ERR_UNSUPPORTED", 3: "FB_E
           4: "FB_ERR_CACHE_INVALID", 5: "FB_ERR_HIP"}
 FB_FLAG_CHECK_CACHE = 1   # fb_shape.flags: debug check that every reused cache row was written
 EXPORTS = ("fb_status_string", "fb_workspace_size", "fb_prefix_attn", "fb_block_attn", "fb_lse_merge",
-           "fb_step", "fb_step_threshold", "fb_mask_threshold", "fb_mask_similarity", "fb_head_cosine", "losa_meta_bytes",
+           "fb_step", "fb_step_threshold", "fb_step_noalloc", "fb_mask_threshold", "fb_mask_similarity", "fb_head_cosine", "losa_meta_bytes",
            "losa_workspace_size", "losa_union_capacity", "losa_page_meta", "losa_select_union", "losa_step",
            "fb_residual_workspace_size", "fb_residual_step", "fb_append_block", "losa_page_meta_append",
            "fb_block_workspace_size", "fb_block_run", "fb_prefix_attn_varlen_workspace_size",
@@ -85,6 +85,7 @@ def load(path: str | None = None):
         "fb_block_attn": (i32, [sp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "fb_lse_merge": (i32, [i64, i32, vp, vp, vp, vp, vp, i32, vp, vp]),
         "fb_step": (i32, [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, tp, vp]),
+        "fb_step_noalloc": (i32, [sp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "fb_step_threshold": (i32, [sp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, tp, vp]),
         "fb_mask_threshold": (i32, [vp, i32, i32, i32, vp, vp]),
         "fb_mask_similarity": (i32, [vp, f32, i64, vp, vp]),
@@ -197,6 +198,13 @@ def step(shape, q, k, v, k_blk, v_blk, reuse_mask, cache_a, cache_l, a_full, l_f
                           _ptr(cache_a), _ptr(cache_l), _ptr(a_full), _ptr(l_full), _ptr(ws),
                           0 if ws is None else ws.numel() * ws.element_size(),
                           None if trace is None else C.byref(trace), _stream(stream)), "fb_step")
+
+
+def step_noalloc(shape, q, k, v, k_blk, v_blk, reuse_mask, cache_a, cache_l, a_full, l_full, stream=None):
+    """fb_step without a workspace: the partials go to the library's static per-GPU array."""
+    _check(load().fb_step_noalloc(C.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(k_blk), _ptr(v_blk),
+                                  _ptr(reuse_mask), _ptr(cache_a), _ptr(cache_l), _ptr(a_full), _ptr(l_full),
+                                  _stream(stream)), "fb_step_noalloc")
 
 
 def step_threshold(shape, q, k, v, k_blk, v_blk, m_updated, tau, cache_a, cache_l, a_full, l_full, ws,

@@ -18,7 +18,7 @@ OBJ = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(HERE, "libflashblock.so")
 CEILING_LIB = os.path.join(HERE, "libfb_ceiling.so")
 CEILING_SOURCES = ["fb_ceiling.hip"]
-SOURCES = ["fb_attn.hip", "fb_stream.hip", "fb_fa.hip", "fb_combine.hip", "fb_losa.hip", "fb_residual.hip", "fb_lifecycle.hip", "fb_api.hip"]
+SOURCES = ["fb_attn.hip", "fb_stream.hip", "fb_fa.hip", "fb_combine.hip", "fb_losa.hip", "fb_residual.hip", "fb_lifecycle.hip", "fb_api.hip", "fb_noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -164,6 +164,26 @@ fb_status fb_step_threshold(const fb_shape* s, const void* q, const void* k, con
                             float* l_full, void* ws, size_t ws_bytes, const fb_trace* trace,
                             hipStream_t stream);
 
+/* Bytes of the static device array that fb_step_noalloc uses on each GPU (64 MiB). */
+#define FB_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* fb_step for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments, results and
+ * errors as fb_step, without the workspace and the timing hooks: the split-KV partial
+ * results go to a static device array of FB_NOALLOC_SCRATCH_BYTES that the library holds
+ * on every GPU it runs on until the process ends.  A shape whose fb_workspace_size() is
+ * larger returns FB_ERR_WORKSPACE and writes nothing (the dLLM step with a 32768-token
+ * prefix and 32 heads needs about 4 MiB).  The call allocates nothing: no hipMalloc,
+ * hipFree or allocating library routine.  On its first call on a device the library
+ * looks up the array's address there (with that device current) and keeps it.  Every call
+ * on one GPU shares that GPU's array, which keeps the last call's contents; nothing in it
+ * needs to start at zero.  Calls that overlap on one GPU (other streams, other threads)
+ * race on the array: the caller serialises them. */
+fb_status fb_step_noalloc(const fb_shape* s, const void* q, const void* k, const void* v,
+                          const void* k_blk, const void* v_blk, const uint8_t* reuse_mask,
+                          float* cache_a, float* cache_l, void* a_full, float* l_full,
+                          hipStream_t stream);
+
 /* Threshold reuse rule [FB-pt §2]: mask[b][h] = (m_updated[b] < tau) for every h.
  * m_updated: device int32 [batch] (tokens updated since the previous step). */
 fb_status fb_mask_threshold(const int32_t* m_updated, int32_t tau, int32_t batch,

@@ -91,6 +91,19 @@ def test_step_rejects_bad_pointers(over, code):
     assert call_step(dllm_shape(), **over) == code
 
 
+def test_step_noalloc_refuses_before_launch():
+    """fb_step_noalloc: an invalid shape returns fb_step's error and a shape whose workspace
+    is larger than the static array returns FB_ERR_WORKSPACE, both before any device call."""
+    lib = fb.load()
+    p = lambda x: C.c_void_p(x)
+    args = [p(0x10000)] * 5 + [None] + [p(0x10000)] * 3 + [None, None]
+    bad = dllm_shape(h_kv=3)
+    assert lib.fb_step_noalloc(C.byref(bad), *args) == 1
+    big = fb.make_shape(1, 12, 12, 128, 4680, seqlen_k=32760)   # about 84 MiB of partials
+    assert fb.workspace_size(big) > 64 << 20
+    assert lib.fb_step_noalloc(C.byref(big), *args) == 3
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(h_kv=3), 1), (dict(batch=0), 1), (dict(block=0), 1), (dict(head_dim=96), 2),
     (dict(flags=2), 1), (dict(flags=3), 1), (dict(num_splits=-1), 1), (dict(seqlen_k=-5), 1), (dict(softmax_scale=-1.0), 1),
