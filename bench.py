@@ -444,9 +444,11 @@ def main():
 
 def measured_ceilings(nbytes: int):
     """The rates this chip reaches on the two resources the attention kernels are bound by,
-    measured here beside the published peaks: a streaming read of `nbytes` (one launch at a
-    time, each timed with events, as the attention kernel is) and a register-only bf16 MFMA
-    loop on every CU (2 workgroups of 4 waves per CU, about 2 ms per launch)."""
+    measured here beside the published peaks: a streaming read of `nbytes` with plain and with
+    non-temporal loads (one launch at a time, each timed with events, as the attention kernel
+    is), and a register-only bf16 MFMA loop on every CU (2 workgroups of 4 waves per CU,
+    about 2 ms per launch).  Also how far MFMA work of one wave and vector work (exp and fma,
+    4 per MFMA, the softmax mix) of another overlap on one SIMD."""
     import torch
     from cached_kv_prefix_amd import ceiling
     ceiling.load()
@@ -454,17 +456,21 @@ def measured_ceilings(nbytes: int):
     buf.fill_(0x01010101)
     wgs = 4096
     sink = torch.empty((wgs, 4), dtype=torch.int32, device="cuda")
-    for _ in range(3):
-        ceiling.stream_read(buf, nbytes, wgs, sink)
-    times = []
-    for _ in range(20):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        ceiling.stream_read(buf, nbytes, wgs, sink)
-        e1.record()
-        times.append((e0, e1))
-    torch.cuda.synchronize()
-    read_s = float(np.mean([a.elapsed_time(b) for a, b in times])) * 1e-3
+
+    def read_us(nt):
+        for _ in range(3):
+            ceiling.stream_read(buf, nbytes, wgs, sink, nontemporal=nt)
+        times = []
+        for _ in range(20):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            ceiling.stream_read(buf, nbytes, wgs, sink, nontemporal=nt)
+            e1.record()
+            times.append((e0, e1))
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in times])) * 1e3
+
+    plain_us, nt_us = read_us(False), read_us(True)
     del buf, sink
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     mwg, iters = 2 * n_cu, 16384
@@ -479,10 +485,46 @@ def measured_ceilings(nbytes: int):
         torch.cuda.synchronize()
         rates.append(ceiling.mfma_flops(mwg, iters) / (e0.elapsed_time(e1) * 1e-3) / 1e12)
     assert (msink.cpu().numpy() == np.float32(64 * iters)).all(), "MFMA loop result"
-    return {"stream_read_GBps": nbytes / read_s / 1e9, "stream_read_us": read_s * 1e6, "stream_read_bytes": nbytes,
+    coissue = mfma_valu_overlap(n_cu)
+    best_us = min(plain_us, nt_us)
+    return {"stream_read_GBps": nbytes / (best_us * 1e-6) / 1e9, "stream_read_us": best_us,
+            "stream_read_plain_GBps": nbytes / (plain_us * 1e-6) / 1e9, "stream_read_plain_us": plain_us,
+            "stream_read_nontemporal_GBps": nbytes / (nt_us * 1e-6) / 1e9, "stream_read_nontemporal_us": nt_us,
+            "stream_read_bytes": nbytes,
             "mfma_bf16_TFLOPs": float(np.median(rates)), "mfma_workgroups": mwg,
-            "probe": "libfb_ceiling.so: grid-stride 16-byte reads (4096 x 256 threads); "
-                     "4 independent v_mfma_f32_32x32x16_bf16 chains per wave"}
+            "mfma_valu_coissue": coissue,
+            "probe": "libfb_ceiling.so: grid-stride 16-byte reads (4096 x 256 threads), plain and non-temporal, "
+                     "the faster one taken as the read ceiling; 4 independent v_mfma_f32_32x32x16_bf16 chains per "
+                     "wave; fbc_mfma_valu for the co-issue"}
+
+
+def mfma_valu_overlap(n_cu: int, k: int = 4, rounds: int = 8192):
+    """Launch times of fbc_mfma_valu's four modes, one workgroup per CU: the MFMA stream alone
+    (one wave per SIMD), the vector stream alone, both side by side (two waves per SIMD) and
+    both interleaved in one wave.  `overlap` = (t_mfma + t_valu - t_pair) / min(t_mfma, t_valu):
+    1 when the shorter stream hides entirely under the longer, 0 when they add up."""
+    import torch
+    from cached_kv_prefix_amd import ceiling
+    sink = torch.empty((n_cu, 8), device="cuda")
+    out = {"valu_per_mfma": k, "rounds": rounds, "workgroups": n_cu}
+    for mode in ("mfma", "valu", "pair", "interleaved"):
+        ceiling.mfma_valu(mode, k, n_cu, 64, sink)
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            ceiling.mfma_valu(mode, k, n_cu, rounds, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        got = sink.cpu().numpy()
+        for j, want in enumerate(ceiling.mfma_valu_expected(mode, rounds)):
+            if want is not None:
+                assert (got[:, j] == np.float32(want)).all(), f"fbc_mfma_valu {mode} result"
+        out[f"{mode}_us"] = float(np.median(ts))
+    t_m, t_v, t_p = out["mfma_us"], out["valu_us"], out["pair_us"]
+    out["overlap"] = (t_m + t_v - t_p) / min(t_m, t_v)
+    return out
 
 
 def context_sweep(fb, args, lengths=(102400, 204800, 409600, 819200)):

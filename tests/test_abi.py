@@ -273,15 +273,26 @@ def test_ceiling_argument_checks_launch_nothing():
     from cached_kv_prefix_amd import ceiling
     lib = ceiling.load()
     buf, sink = C.c_void_p(0x10000), C.c_void_p(0x20000)
-    assert lib.fbc_stream_read(None, 1024, 4, sink, None) == 1
-    assert lib.fbc_stream_read(buf, 1024, 4, None, None) == 1
-    assert lib.fbc_stream_read(buf, 0, 4, sink, None) == 1
-    assert lib.fbc_stream_read(buf, 1000, 4, sink, None) == 1          # not a multiple of 16 bytes
-    assert lib.fbc_stream_read(buf, 1024, 0, sink, None) == 1
-    assert lib.fbc_stream_read(buf, 1024, 65537, sink, None) == 1
-    assert lib.fbc_stream_read(C.c_void_p(0x10008), 1024, 4, sink, None) == 1   # misaligned
+    assert lib.fbc_stream_read(None, 1024, 4, 0, sink, None) == 1
+    assert lib.fbc_stream_read(buf, 1024, 4, 0, None, None) == 1
+    assert lib.fbc_stream_read(buf, 0, 4, 0, sink, None) == 1
+    assert lib.fbc_stream_read(buf, 1000, 4, 0, sink, None) == 1          # not a multiple of 16 bytes
+    assert lib.fbc_stream_read(buf, 1024, 0, 0, sink, None) == 1
+    assert lib.fbc_stream_read(buf, 1024, 65537, 0, sink, None) == 1
+    assert lib.fbc_stream_read(C.c_void_p(0x10008), 1024, 4, 0, sink, None) == 1   # misaligned
     assert lib.fbc_mfma_loop(4, 10, 1.0, 1.0, None, None) == 1
     assert lib.fbc_mfma_loop(0, 10, 1.0, 1.0, sink, None) == 1
     assert lib.fbc_mfma_loop(65537, 10, 1.0, 1.0, sink, None) == 1
     assert lib.fbc_mfma_loop(4, 0, 1.0, 1.0, sink, None) == 1
     assert lib.fbc_mfma_loop(4, 262145, 1.0, 1.0, sink, None) == 1
+    assert lib.fbc_stream_read(buf, 1024, 4, 2, sink, None) == 1       # nontemporal is 0 or 1
+    assert lib.fbc_mfma_valu(0, 0, 4, 10, 1.0, None, None) == 1
+    assert lib.fbc_mfma_valu(4, 4, 4, 10, 1.0, sink, None) == 1        # no such mode
+    assert lib.fbc_mfma_valu(-1, 4, 4, 10, 1.0, sink, None) == 1
+    assert lib.fbc_mfma_valu(2, 0, 4, 10, 1.0, sink, None) == 1        # a vector stream needs operations
+    assert lib.fbc_mfma_valu(1, 3, 4, 10, 1.0, sink, None) == 1
+    assert lib.fbc_mfma_valu(3, 16, 4, 10, 1.0, sink, None) == 1
+    assert lib.fbc_mfma_valu(2, 4, 0, 10, 1.0, sink, None) == 1
+    assert lib.fbc_mfma_valu(2, 4, 65537, 10, 1.0, sink, None) == 1
+    assert lib.fbc_mfma_valu(2, 4, 4, 0, 1.0, sink, None) == 1
+    assert lib.fbc_mfma_valu(2, 4, 4, 262145, 1.0, sink, None) == 1

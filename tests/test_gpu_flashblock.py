@@ -119,6 +119,48 @@ def test_prefix_and_block_attn(gpu_lib, case):
     check_lse(np_of(l), el, dt, f"{name} L_in")
 
 
+# Groups of more than 128 rows run on the phase-shifted 8-wave kernel: one key tile, a full
+# single tile, two tiles, ragged tails on both the key and the query side, empty waves in
+# the last query tile, many splits, peaked logits (the lazy max is raised mid-chunk), and
+# two heads of very different scale in one launch.
+WIDE_CASES = [
+    # name, batch, h_q, h_kv, B, seqlens, num_splits, q scale
+    ("one_partial_tile", 1, 1, 1, 256, [40], 0, 1.0),
+    ("one_full_tile", 1, 2, 2, 200, [64], 0, 1.0),
+    ("two_tiles", 1, 1, 1, 257, [128], 0, 1.0),
+    ("rows512_tail_keys", 1, 1, 1, 512, [1333], 0, 1.0),
+    ("rows_tail_33", 2, 2, 2, 289, [700, 96], 0, 1.0),
+    ("many_splits", 1, 2, 1, 150, [2000], 7, 1.0),
+    ("peaked", 1, 2, 2, 300, [1500], 0, 4.0),
+    ("gqa4_rows_per_wave_cross_heads", 1, 8, 2, 70, [900], 3, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=[c[0] for c in WIDE_CASES])
+def test_wide_groups_prefix_and_block(gpu_lib, case):
+    import torch
+    fb = gpu_lib
+    name, b, hq, hkv, B, lens, ns, qs = case
+    say(f"[wide groups] {name}")
+    p = synth.custom(19, b, hq, hkv, 128, B, lens, std=1.0)
+    p.q *= qs   # a power of two: the values stay bf16
+    dev = to_device_guarded(p)
+    shape = _shape(fb, p, dev, varlen=True, num_splits=ns)
+    ws = _ws(fb, shape)
+    a = guarded((b, B, hq, 128), torch.float32, float("nan"), "a_out")
+    l = guarded((b, B, hq), torch.float32, float("nan"), "l_out")
+    fb.prefix_attn(shape, dev["q"], dev["k"], dev["v"], a, l, ws)
+    torch.cuda.synchronize()
+    ea, el = prefix_attention(p.q, p.k, p.v, p.cu, hkv, p.scale)
+    check_attn(np_of(a), ea, "bf16", f"{name} A_out")
+    check_lse(np_of(l), el, "bf16", f"{name} L_out")
+    fb.block_attn(shape, dev["q"], dev["k_blk"], dev["v_blk"], a, l, ws)
+    torch.cuda.synchronize()
+    ea, el = block_attention(p.q, p.k_blk, p.v_blk, p.scale)
+    check_attn(np_of(a), ea, "bf16", f"{name} A_in")
+    check_lse(np_of(l), el, "bf16", f"{name} L_in")
+
+
 def test_prefix_peaked_softmax(gpu_lib):
     """Q, K ~ N(0, 1) at d = 128: logits of std ~1 make the softmax peaked, so errors in the
     max/sum bookkeeping show up."""
