@@ -16,10 +16,9 @@
 //     current one is computed, then written to the other LDS buffer; one barrier per tile;
 //   * groups of more than 128 rows (W = 8, matrix-bound): software pipeline, S of tile
 //     t + 1 is issued before the softmax of tile t, so the matrix instructions and the
-//     vector softmax of one wave are independent.  Measured on MI355X: the matrix core
-//     and the vector ALU of one SIMD overlap only partly within a wave and not across
-//     waves, so the softmax (about half the matrix time) mostly adds to it; the kernel
-//     reaches about 40% of the bf16 peak, the matrix work alone 85%;
+//     vector softmax of one wave are independent.  The two waves of a SIMD run the same
+//     mix in step (one barrier per tile), so the softmax (about half the matrix time)
+//     mostly adds to the matrix work: the kernel reaches about 0.4 of the bf16 peak;
 //   * groups of 33-128 rows (W = 4, DEEP, memory-bound): no score pipelining, two tiles of
 //     loads in flight (two register staging sets);
 //   * a paged source (DEEP only, power-of-two pages): the chunk's page list is staged in
