@@ -73,6 +73,14 @@ SMALL = [
     ("block300_rank_own_launch", 1, 2, 2, 64, 300, [500], 5, 16, 6, "bf16"),
     # top-k above 256: the selection runs over all keys (no threshold from the thread maxima)
     ("topk300_over_all_keys", 1, 2, 2, 64, 8, [1000], 2, 1, 300, "bf16"),
+    # every block token active (no stable rows)
+    ("all_active", 1, 2, 2, 64, 8, [300], 8, 16, 4, "bf16"),
+    # one sequence with an empty prefix: no pages, an empty union, the cache stays (0, -inf)
+    ("empty_prefix_sequence", 2, 4, 2, 64, 8, [0, 200], 3, 16, 4, "bf16"),
+    # a page size that is not a power of two (token = page * 12 + offset)
+    ("page12", 1, 4, 2, 128, 16, [777], 3, 12, 6, "bf16"),
+    # 4 query heads x 8 active tokens = 32 rows per KV head, the most the streaming pass takes
+    ("gqa4_32_active_rows", 1, 8, 2, 128, 32, [2000], 8, 16, 16, "bf16"),
 ]
 
 
