@@ -527,6 +527,35 @@ def mfma_valu_overlap(n_cu: int, k: int = 4, rounds: int = 8192):
     return out
 
 
+def sdpa_reference(dev, p, flop):
+    """torch's scaled_dot_product_attention, flash backend only, on the all-fresh video
+    computation (every block query over prefix + block keys, the bf16 inputs above), timed
+    as a reference for what a library attention reaches on this shape.  Only the flash
+    backend is allowed (no fallback to the math path).  None when it is not available."""
+    import torch
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        q = dev["q"][0].transpose(0, 1).contiguous().unsqueeze(0)                       # [1, h, B, d]
+        k = torch.cat([dev["k"], dev["k_blk"][0]], 0).transpose(0, 1).contiguous().unsqueeze(0)
+        v = torch.cat([dev["v"], dev["v_blk"][0]], 0).transpose(0, 1).contiguous().unsqueeze(0)
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            for _ in range(2):
+                torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=p.scale)
+            ts = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=p.scale)
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+        del q, k, v
+        us = float(np.median(ts))
+        return {"us": us, "TFLOPs": flop / (us * 1e-6) / 1e12, "frac_mfma": flop / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+    except Exception as e:   # no flash kernel in this torch build
+        return {"us": None, "error": type(e).__name__}
+
+
 def context_sweep(fb, args, lengths=(102400, 204800, 409600, 819200)):
     """Prefix lengths 100k -> 800k on the dLLM step shape (32 heads, d 128, B 32, bf16):
     the always-fresh step and the mean step of an 8-step block under the threshold rule
@@ -712,6 +741,7 @@ def other_workloads(fb, args, keep=None):
                           "attn_kernel_all_fresh_us": a_all * 1e6,
                           "attn_kernel_all_fresh_frac_mfma": f_all / a_all / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                           "fresh_heads": n_fresh, "tokens_per_s": nq / w_m}
+    out["video_block"]["torch_sdpa_flash_all_fresh"] = sdpa_reference(dev, p, f_all)
     del dev, bufs
     # LoSA sparse step
     p, dev, shape, bufs, ls, sparse, sel, cap = losa_setup(fb)
