@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--only-video", choices=["masked", "fresh"], default=None,
                     help="video-block steps only, masked (7 of 12 heads reuse) or all fresh, one JSON line of "
                          "their time (for profiling)")
+    ap.add_argument("--video-splits", action="store_true",
+                    help="video-block masked and all-fresh steps at forced prefix split counts (2, 5, 8, 16) and "
+                         "at the plan's own, one JSON line (for the split-plan evidence)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one device copy of this many MiB first (counter calibration)")
@@ -367,6 +370,9 @@ def main():
         return
     if args.only_video:
         print(json.dumps({"only_video": only_video(fb, args, args.only_video)}))
+        return
+    if args.video_splits:
+        print(json.dumps({"video_splits": video_splits(fb, args)}))
         return
 
     # ---------------------------------------------------------------- headline workload
@@ -821,6 +827,39 @@ def only_video(fb, args, which):
     sim = torch.from_numpy(p.extra["sim"]).cuda() if which == "masked" else None
     w = wall_time(lambda tr: run_step(fb, shape, dev, bufs, None, sim=sim), args.steps, args.warmup)
     return {"which": which, "step_us": w * 1e6}
+
+
+def video_splits(fb, args, counts=(0, 2, 5, 8, 16)):
+    """The video-block masked step (7 of 12 heads reuse) and all-fresh step with the prefix
+    pass forced to `counts` splits per head through fb_shape.num_splits (0 = the split plan's
+    own choice), `steps` timed steps each after `warmup`: wall time per step and the event
+    time of the attention kernel (the smaller of the two, as in other_workloads)."""
+    import torch
+    import synth
+    from synth.device import to_device
+    p = synth.video()
+    dev = to_device(p)
+    sim = torch.from_numpy(p.extra["sim"]).cuda()
+    # untimed warm-up on the plan's own split count, so that the first row does not carry
+    # the clock ramp of a cold GPU
+    shape = fb.make_shape(p.batch, p.h_q, p.h_kv, p.d, p.B, seqlen_k=int(p.seqlens[0]))
+    _, bufs = setup_step(fb, p, dev)
+    wall_time(lambda tr: run_step(fb, shape, dev, bufs, None, sim=sim), 30, 5)
+    del bufs
+    rows = []
+    for ns in counts:
+        shape = fb.make_shape(p.batch, p.h_q, p.h_kv, p.d, p.B, seqlen_k=int(p.seqlens[0]), num_splits=ns)
+        _, bufs = setup_step(fb, p, dev)
+        bufs["ws"] = torch.empty(fb.workspace_size(shape), dtype=torch.uint8, device="cuda")
+        w_m, a_m, _ = time_steps(lambda tr: run_step(fb, shape, dev, bufs, None, sim=sim, trace=tr), args.steps,
+                                 args.warmup)
+        bufs["mask"].zero_()
+        w_f, a_f, _ = time_steps(lambda tr: run_step(fb, shape, dev, bufs, None, trace=tr), args.steps, args.warmup)
+        rows.append({"num_splits": ns, "masked_step_us": w_m * 1e6, "masked_attn_us": min(a_m, w_m) * 1e6,
+                     "fresh_step_us": w_f * 1e6, "fresh_attn_us": min(a_f, w_f) * 1e6,
+                     "workspace_bytes": fb.workspace_size(shape)})
+        del bufs
+    return rows
 
 
 def residual_workload(fb, p, dev, shape, sel, cap, steps, short_steps):
